@@ -1,0 +1,390 @@
+"""Plain, slow, fp64 CPU oracle of the S3R hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by ``__graft_entry__.smoke()`` and
+by the ``cpu_baseline`` leg of bench.py, never by the library or its binding.
+It shares no code with the HIP path.
+
+What is computed, and where it comes from
+-----------------------------------------
+"S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
+Abstract: tokens are drafted with *sparse attention*, the response is produced by
+*full-attention verification* and *exact speculative sampling*, draft and verify
+share one set of parameters (so one KV cache serves both), and dense
+verification needs the *complete* KV history. The pages give no equations, so
+every step below is the plain definition of the operation, written out:
+
+* page bounds / page select: the pages leave the sparse rule open; this library
+  fixes a query-aware rule after the Quest title the page-3 reference list
+  cites ("Quest: Query-Aware Sparsity ..."): per page elementwise key min/max,
+  an upper bound on each query head's logit, top-k pages under a token budget.
+* attention: softmax(scale * q K^T) V over a token set (textbook definition),
+  paged as in the PagedAttention title of the same list.
+* spec sample: the accept/residual rule of the two speculative-sampling titles
+  the page-3 list cites ("Fast Inference from Transformers via Speculative
+  Decoding"; "Accelerating Large Language Model Decoding with Speculative
+  Sampling"): accept x with prob min(1, p(x)/q(x)), otherwise draw from
+  norm(max(0, p - q)); a bonus draw from the last target row if all accept.
+* RNG: Philox4x64-10 from Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:
+  As Easy as 1, 2, 3" (SC'11), written from that definition.
+
+Pins (tests/test_oracle_*.py): brute-force bounds and sort, torch SDPA on CPU,
+a second streaming-softmax decode path, exact rational enumeration of the
+sampler at vocab 8, chi-square Monte Carlo, q = p => full acceptance, the
+accepted-length law prod(alpha_i), and numpy.random.Philox known answers.
+Parity of the page-level figures (attention share, end-to-end speedup) is
+unpinned: they need the model and workloads the pages measured.
+
+Data layout (a format both sides must agree on):
+  k_pool[N_phys][Hkv][P][D]   key of token t in page slot t % P
+  v_pool[N_phys][Hkv][D][P]   value, transposed inside each page
+  page_table[B][max_pages]    logical page -> physical page
+  seq_lens[B]                 KV positions visible to the last query
+  bounds[N_phys][Hkv][2][D]   [0] = elementwise min, [1] = elementwise max
+Every physical page belongs to one sequence. Inputs are numpy arrays; bf16 data
+is passed as its exact float64 upcast.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "PHILOX_M0", "PHILOX_M1", "PHILOX_W0", "PHILOX_W1",
+    "philox4x64_10", "uniform",
+    "key_row", "value_row", "n_pages",
+    "page_bounds", "page_scores", "page_select",
+    "attend", "sparse_draft_attn", "dense_verify_attn", "decode_streaming",
+    "softmax", "icdf", "spec_sample", "draw_draft_tokens",
+]
+
+# ---------------------------------------------------------------------------
+# Philox4x64-10 (Salmon et al., SC'11): 4x64-bit counter, 2x64-bit key, ten
+# rounds of two 64x64->128 multiplies, key bumped by the two Weyl constants
+# between rounds.
+# ---------------------------------------------------------------------------
+PHILOX_M0 = 0xD2E7470EE14C6C93
+PHILOX_M1 = 0xCA5A826395121157
+PHILOX_W0 = 0x9E3779B97F4A7C15  # golden ratio
+PHILOX_W1 = 0xBB67AE8584CAA73B  # sqrt(3) - 1
+_MASK64 = (1 << 64) - 1
+
+
+def philox4x64_10(counter, key):
+    """Return the four 64-bit output words for one (counter, key) block."""
+    x0, x1, x2, x3 = (int(c) & _MASK64 for c in counter)
+    k0, k1 = (int(k) & _MASK64 for k in key)
+    for _ in range(10):
+        prod0 = PHILOX_M0 * x0
+        prod1 = PHILOX_M1 * x2
+        hi0, lo0 = prod0 >> 64, prod0 & _MASK64
+        hi1, lo1 = prod1 >> 64, prod1 & _MASK64
+        x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
+        k0 = (k0 + PHILOX_W0) & _MASK64
+        k1 = (k1 + PHILOX_W1) & _MASK64
+    return x0, x1, x2, x3
+
+
+def uniform(seed, offset, b, slot, stream):
+    """U(b, slot, stream) in [0, 1): the top 53 bits of word 0, times 2^-53.
+
+    key = (seed, 0), counter = (offset, b, slot, stream). Stream 0 holds the
+    accept uniforms, stream 1 the residual/bonus draws, stream 2 the draft-token
+    draws a drafter makes upstream of the sampler.
+    """
+    w0 = philox4x64_10((offset, b, slot, stream), (seed, 0))[0]
+    return (w0 >> 11) * (2.0 ** -53)
+
+
+# ---------------------------------------------------------------------------
+# Paged KV access
+# ---------------------------------------------------------------------------
+def n_pages(seq_len, P):
+    return -(-int(seq_len) // P)
+
+
+def key_row(k_pool, page_table, b, h, t):
+    P = k_pool.shape[2]
+    return k_pool[page_table[b, t // P], h, t % P, :]
+
+
+def value_row(v_pool, page_table, b, h, t):
+    P = v_pool.shape[3]
+    return v_pool[page_table[b, t // P], h, :, t % P]
+
+
+# ---------------------------------------------------------------------------
+# Page bounds and query-aware page selection
+# ---------------------------------------------------------------------------
+def page_bounds(k_pool, page_table, seq_lens, seqs=None):
+    """bounds[phys][h][0|1][d] = min|max over the page's valid tokens of K[t][h][d].
+
+    Valid tokens of logical page j of sequence b: j*P <= t < min((j+1)*P, seq_len).
+    Physical pages not reached by any (b, j) are left as NaN.
+    """
+    n_phys, hkv, P, D = k_pool.shape
+    out = np.full((n_phys, hkv, 2, D), np.nan)
+    B = page_table.shape[0]
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        for j in range(n_pages(L, P)):
+            phys = page_table[b, j]
+            for h in range(hkv):
+                rows = np.stack([key_row(k_pool, page_table, b, h, t)
+                                 for t in range(j * P, min((j + 1) * P, L))])
+                out[phys, h, 0] = rows.min(axis=0)
+                out[phys, h, 1] = rows.max(axis=0)
+    return out
+
+
+def page_scores(bounds, q, page_table, seq_lens, scale, b, h, P=16):
+    """Scores of every logical page of (sequence b, kv head h).
+
+    score_j = max over the q heads g of the group of
+              scale * sum_d max(q[g,d] * kmin[j,d], q[g,d] * kmax[j,d]),
+    an upper bound on scale * q_g . k_t for every token t of page j. One
+    selection per kv head lets the whole query group share the pages it reads.
+    q: [B][Hq][D].
+    """
+    hkv = bounds.shape[1]
+    G = q.shape[1] // hkv
+    n = n_pages(int(seq_lens[b]), P)
+    scores = np.empty(n)
+    for j in range(n):
+        kmin = bounds[page_table[b, j], h, 0]
+        kmax = bounds[page_table[b, j], h, 1]
+        best = -math.inf
+        for g in range(h * G, (h + 1) * G):
+            s = scale * float(np.sum(np.maximum(q[b, g] * kmin, q[b, g] * kmax)))
+            best = max(best, s)
+        scores[j] = best
+    return scores
+
+
+def page_select(bounds, q, page_table, seq_lens, budget_tokens, scale, P=16, seqs=None):
+    """Top-k pages per (sequence, kv head) under a token budget.
+
+    k = budget_tokens // P (a partial tail page costs a full page). With n pages
+    in the sequence: if k >= n every page is taken; otherwise pages are ranked by
+    (score descending, logical index ascending) and the first k kept. The kept
+    indices are emitted in ascending order and padded with -1 to length k.
+
+    Returns (selected[B][Hkv][k] int32, num_selected[B] int32, scores) where
+    scores[(b, h)] holds every page score (None when k >= n).
+    """
+    B = page_table.shape[0]
+    hkv = bounds.shape[1]
+    k = budget_tokens // P
+    selected = np.full((B, hkv, k), -1, dtype=np.int32)
+    num_selected = np.zeros(B, dtype=np.int32)
+    scores = {}
+    for b in (range(B) if seqs is None else seqs):
+        n = n_pages(int(seq_lens[b]), P)
+        num_selected[b] = min(k, n)
+        for h in range(hkv):
+            if k >= n:
+                selected[b, h, :n] = np.arange(n)
+                scores[(b, h)] = None
+                continue
+            sc = page_scores(bounds, q, page_table, seq_lens, scale, b, h, P)
+            order = sorted(range(n), key=lambda j: (-sc[j], j))
+            selected[b, h, :] = sorted(order[:k])
+            scores[(b, h)] = sc
+    return selected, num_selected, scores
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def attend(qv, Kt, Vt, scale):
+    """softmax(scale * Kt @ qv) @ Vt, the textbook definition, in fp64.
+
+    An empty token set (a sequence or causal row that sees no position) has no
+    softmax; the library defines its output as zeros, and so does the oracle.
+    """
+    if len(Kt) == 0:
+        return np.zeros(Vt.shape[1] if np.ndim(Vt) == 2 else 0)
+    logits = scale * (Kt @ qv)
+    m = logits.max()
+    w = np.exp(logits - m)
+    return (w / w.sum()) @ Vt
+
+
+def _gather(k_pool, v_pool, page_table, b, h, positions):
+    positions = list(positions)
+    D = k_pool.shape[3]
+    if not positions:
+        return np.zeros((0, D)), np.zeros((0, D))
+    Kt = np.stack([key_row(k_pool, page_table, b, h, t) for t in positions])
+    Vt = np.stack([value_row(v_pool, page_table, b, h, t) for t in positions])
+    return Kt, Vt
+
+
+def sparse_draft_attn(q, k_pool, v_pool, page_table, seq_lens, selected, scale,
+                      seqs=None, heads=None):
+    """Single-query GQA decode over the selected pages only.
+
+    q: [B][Hq][D]; selected: [B][Hkv][k] logical page ids (-1 = unused). Query
+    head g reads kv head g // G over T = {t < seq_len : t // P in sel(b, h)}.
+    Returns out[B][Hq][D] (NaN where not computed).
+    """
+    B, Hq, D = q.shape
+    hkv = k_pool.shape[1]
+    P = k_pool.shape[2]
+    G = Hq // hkv
+    out = np.full((B, Hq, D), np.nan)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        for g in (range(Hq) if heads is None else heads):
+            h = g // G
+            pages = sorted({int(j) for j in selected[b, h] if j >= 0})
+            positions = [t for j in pages for t in range(j * P, min((j + 1) * P, L))]
+            Kt, Vt = _gather(k_pool, v_pool, page_table, b, h, positions)
+            out[b, g] = attend(q[b, g], Kt, Vt, scale)
+    return out
+
+
+def dense_verify_attn(q, k_pool, v_pool, page_table, seq_lens, scale,
+                      seqs=None, heads=None):
+    """Causal attention of nq query positions over the complete paged KV.
+
+    q: [B][nq][Hq][D]. Query i sits at position seq_len - nq + i and sees every
+    position <= its own. Returns out[B][nq][Hq][D] (NaN where not computed).
+    """
+    B, nq, Hq, D = q.shape
+    hkv = k_pool.shape[1]
+    G = Hq // hkv
+    out = np.full((B, nq, Hq, D), np.nan)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        for g in (range(Hq) if heads is None else heads):
+            h = g // G
+            Kt, Vt = _gather(k_pool, v_pool, page_table, b, h, range(max(L, 0)))
+            for i in range(nq):
+                visible = max(0, L - nq + i + 1)
+                out[b, i, g] = attend(q[b, i, g], Kt[:visible], Vt[:visible], scale)
+    return out
+
+
+def decode_streaming(qv, k_pool, v_pool, page_table, b, h, n_visible, scale):
+    """A second, independent decode path: one token at a time, running max/sum.
+
+    o_n = (sum_{t<n} e^{s_t - m_n} v_t) / (sum_{t<n} e^{s_t - m_n}), updated per
+    token; used to pin the batched verify against sequential single decodes.
+    """
+    m = -math.inf
+    den = 0.0
+    num = np.zeros(k_pool.shape[3])
+    for t in range(n_visible):
+        s = scale * float(np.dot(key_row(k_pool, page_table, b, h, t), qv))
+        m_new = max(m, s)
+        c = math.exp(m - m_new) if m != -math.inf else 0.0
+        e = math.exp(s - m_new)
+        num = num * c + e * value_row(v_pool, page_table, b, h, t)
+        den = den * c + e
+        m = m_new
+    return num / den if n_visible > 0 else num
+
+
+# ---------------------------------------------------------------------------
+# Exact speculative sampling
+# ---------------------------------------------------------------------------
+def softmax(logits, temperature):
+    z = np.asarray(logits, dtype=np.float64) / temperature
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def icdf(w, u):
+    """Smallest t with sum_{s<=t} w_s > u * sum(w), ascending token order.
+
+    Returns (t, margin): margin is the distance of u*sum(w) from the nearer
+    boundary of the chosen bin, over sum(w). If rounding leaves no such t the
+    last t with w_t > 0 is returned with margin 0.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    total = float(w.sum())
+    target = u * total
+    c = np.cumsum(w)
+    hits = np.nonzero(c > target)[0]
+    if hits.size == 0:
+        return int(np.nonzero(w > 0)[0][-1]), 0.0
+    t = int(hits[0])
+    lo = float(c[t - 1]) if t > 0 else 0.0
+    return t, min(target - lo, float(c[t]) - target) / total
+
+
+def spec_sample(draft_logits, target_logits, draft_tokens, temperature, seed, offset,
+                uniform_fn=None):
+    """One round of exact speculative sampling per sequence.
+
+    draft_logits [B][gamma][V], target_logits [B][gamma+1][V], draft_tokens
+    [B][gamma]. p_i = softmax(target_i / T), q_i = softmax(draft_i / T).
+    For i = 0..gamma-1 with x = draft_tokens[b][i], u = U(b, i, 0):
+      accept iff (q_i(x) > 0 and u < p_i(x) / q_i(x)) or (q_i(x) = 0 and p_i(x) > 0);
+      on reject draw out[i] = ICDF(max(0, p_i - q_i), U(b, i, 1)) (p_i if that
+      residual has no mass) and stop.
+    If all gamma accept, out[gamma] = ICDF(p_gamma, U(b, gamma, 1)).
+
+    Returns (out_tokens[B][gamma+1] int32 with -1 after the last emitted token,
+    num_accepted[B] int32, decisions) where decisions[b] lists
+    (slot, kind, margin) in order: kind "accept" (margin |u - p/q|, inf when
+    q(x) = 0) or "draw" (margin from icdf()).
+
+    uniform_fn(b, slot, stream), when given, replaces the Philox uniforms (used
+    to enumerate the sampler's outcomes exactly in tests).
+    """
+    if uniform_fn is None:
+        def uniform_fn(b, slot, stream):
+            return uniform(seed, offset, b, slot, stream)
+    B, gamma, V = draft_logits.shape
+    out = np.full((B, gamma + 1), -1, dtype=np.int32)
+    n_acc = np.zeros(B, dtype=np.int32)
+    decisions = []
+    for b in range(B):
+        dec = []
+        n = 0
+        rejected = False
+        for i in range(gamma):
+            p = softmax(target_logits[b, i], temperature)
+            q = softmax(draft_logits[b, i], temperature)
+            x = int(draft_tokens[b, i])
+            u = uniform_fn(b, i, 0)
+            if q[x] > 0:
+                ratio = p[x] / q[x]
+                accept = u < ratio
+                dec.append((i, "accept", abs(u - ratio)))
+            else:
+                accept = p[x] > 0
+                dec.append((i, "accept", math.inf))
+            if accept:
+                out[b, i] = x
+                n += 1
+                continue
+            w = np.maximum(0.0, p - q)
+            if w.sum() == 0.0:
+                w = p
+            t, margin = icdf(w, uniform_fn(b, i, 1))
+            out[b, i] = t
+            dec.append((i, "draw", margin))
+            rejected = True
+            break
+        if not rejected:
+            p = softmax(target_logits[b, gamma], temperature)
+            t, margin = icdf(p, uniform_fn(b, gamma, 1))
+            out[b, gamma] = t
+            dec.append((gamma, "draw", margin))
+        n_acc[b] = n
+        decisions.append(dec)
+    return out, n_acc, decisions
+
+
+def draw_draft_tokens(draft_logits, temperature, seed, offset):
+    """x[b][i] = ICDF(q_i, U(b, i, 2)): the drafter's own draws from q_i."""
+    B, gamma, _ = draft_logits.shape
+    x = np.empty((B, gamma), dtype=np.int32)
+    for b in range(B):
+        for i in range(gamma):
+            x[b, i] = icdf(softmax(draft_logits[b, i], temperature),
+                           uniform(seed, offset, b, i, 2))[0]
+    return x
