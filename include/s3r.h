@@ -1,0 +1,194 @@
+/*
+ * libs3r: the data-parallel hot path of Self-Sparse Speculative Rollouts on one
+ * MI355X (gfx950).
+ *
+ * "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
+ * Abstract: a rollout round drafts tokens with sparse attention, then produces
+ * the response through full-attention verification and exact speculative
+ * sampling; draft and verify share one set of policy parameters, so both read
+ * the same KV cache, and dense verification reads the complete KV history.
+ * The calls below are that round's per-step operations.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers are device pointers (hipMalloc'd or torch CUDA tensors) unless a
+ *   comment says "host". The caller owns every buffer and keeps it alive until
+ *   the work queued on `stream` has completed. The library allocates and frees
+ *   no device memory; scratch is the caller's `workspace`, sized by the
+ *   matching *_workspace() query (host-only, no HIP call).
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *   only enqueue work: no call synchronises the device or the host.
+ * - Host-side validation of scalars, pointers and shapes happens before any HIP
+ *   call; a failed check returns its status and enqueues nothing. Device data
+ *   (page ids, seq_lens, token ids) is trusted. No C++ exception crosses the
+ *   ABI. The library keeps no state between calls; calls on different streams
+ *   are safe if their outputs and workspaces are disjoint.
+ * - Supported: head_dim 64 or 128, page_size 16, num_q_heads a multiple of
+ *   num_kv_heads with G = num_q_heads/num_kv_heads <= 8, kv dtype f32 or bf16,
+ *   G * n_queries <= 64 attention rows per kv head, 1 <= gamma <= 16.
+ *
+ * Data layout in HBM
+ * ------------------
+ *   k_pool     [num_phys_pages][Hkv][P][D]  key of token t at slot t % P
+ *   v_pool     [num_phys_pages][Hkv][D][P]  value, transposed inside each page
+ *   page_table [B][max_pages_per_seq] int32 logical page -> physical page
+ *   seq_lens   [B] int32                    KV positions visible to the last query
+ *   bounds     [num_phys_pages][Hkv][2][D]  kv dtype; [0] elementwise key min,
+ *                                           [1] elementwise key max of the page
+ * Every physical page belongs to one sequence. A sequence with seq_len <= 0,
+ * and a causal verify row that sees no position, get an all-zero output.
+ */
+#ifndef S3R_H
+#define S3R_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t s3r_status;
+#define S3R_OK 0
+#define S3R_ERR_INVALID_ARGUMENT 1
+#define S3R_ERR_UNSUPPORTED 2
+#define S3R_ERR_WORKSPACE_TOO_SMALL 3
+#define S3R_ERR_HIP 4
+
+typedef enum { S3R_F32 = 0, S3R_BF16 = 1 } s3r_dtype;
+
+/* Host struct describing caller-owned device buffers of one paged KV cache. */
+typedef struct {
+  int32_t num_seqs;          /* B */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv; q head g reads kv head g / (Hq/Hkv) */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t page_size;         /* P: 16 */
+  int32_t max_pages_per_seq; /* row length of page_table */
+  int32_t total_pages_hint;  /* host: sum over sequences of their page count,
+                                or 0 if unknown (then B * max_pages_per_seq is
+                                assumed). Only sizes the split-KV partitioning. */
+  s3r_dtype kv_dtype;        /* dtype of k_pool, v_pool, bounds and q */
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+} s3r_paged_kv;
+
+/* Workspace sizes in bytes (host computation only; 0 means none needed). */
+size_t s3r_page_select_workspace(const s3r_paged_kv* kv, int32_t budget_tokens);
+/* n_queries: 1 for the draft, gamma+1 for verify. max_pages_attended: k
+   (= budget/P) for the draft, max_pages_per_seq for verify. */
+size_t s3r_attn_workspace(const s3r_paged_kv* kv, int32_t n_queries, int32_t max_pages_attended);
+size_t s3r_spec_sample_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab);
+
+/*
+ * s3r_page_bounds_update: recompute the exact elementwise min and max of the
+ * keys of every page touched since the last call, over the page's valid
+ * tokens j*P <= t < min((j+1)*P, seq_len). This keeps the per-page key bounds
+ * that s3r_page_select scores against in step with the KV cache after a KV
+ * append or rollback (support for the query-aware selection rule).
+ *   bounds     out, [num_phys_pages][Hkv][2][D] in kv dtype.
+ *   first_pos  [B] int32: for sequence b, pages from first_pos[b] / P to the
+ *              last page of seq_lens[b] are recomputed. NULL = every page.
+ *   max_pages_touched  host: an upper bound on the pages any sequence has
+ *              touched when first_pos is given (ignored when NULL).
+ * Errors: INVALID_ARGUMENT for NULL kv/pools/page_table/seq_lens/bounds or a
+ * non-positive max_pages_touched with first_pos given.
+ */
+s3r_status s3r_page_bounds_update(const s3r_paged_kv* kv, void* bounds, const int32_t* first_pos,
+                                  int32_t max_pages_touched, void* stream);
+
+/*
+ * s3r_page_select: query-aware page selection for the sparse draft. The S3R
+ * abstract states only that drafting uses sparse attention; this library fixes
+ * the rule, after the Quest work the S3R reference list cites: per (sequence
+ * b, kv head h) with n = ceil(seq_len/P) pages and k = budget_tokens / P,
+ *   score_j = max over the G q heads of h of
+ *             softmax_scale * sum_d max(q_d * kmin_{j,d}, q_d * kmax_{j,d}),
+ * an upper bound on each head's logit for any token of page j. If k >= n all
+ * pages 0..n-1 are taken; otherwise the k best by (score desc, page asc).
+ *   q            [B][Hq][D] kv dtype, the draft query.
+ *   selected     out [B][Hkv][k] int32 logical page ids, ascending, -1 padded.
+ *   num_selected out [B] int32 = min(k, n).
+ * Errors: INVALID_ARGUMENT for NULL pointers or budget_tokens < P;
+ * WORKSPACE_TOO_SMALL if workspace_bytes < s3r_page_select_workspace().
+ * Scores are fp32; ties closer than fp32 rounding may order differently from an
+ * exact computation.
+ */
+s3r_status s3r_page_select(const s3r_paged_kv* kv, const void* bounds, const void* q,
+                           int32_t budget_tokens, float softmax_scale, int32_t* selected,
+                           int32_t* num_selected, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * s3r_sparse_draft_attn: one draft step's attention, over the selected pages
+ * only ("uses sparse attention to propose tokens", S3R Abstract). Query head g
+ * of sequence b attends, with softmax(softmax_scale * q K^T) V, to the tokens
+ * t < seq_len of the pages in selected[b][g / G]. The G heads of a kv head
+ * share each K/V tile they read.
+ *   q         [B][Hq][D] kv dtype.
+ *   selected  [B][Hkv][k] int32 logical page ids in s3r_page_select's format:
+ *             entries equal to -1 are skipped; only the first
+ *             min(k, ceil(seq_len/P)) entries of each row are read.
+ *   out       [B][Hq][D] in out_dtype (f32 or bf16), written, never read.
+ * Errors: INVALID_ARGUMENT / UNSUPPORTED / WORKSPACE_TOO_SMALL as above.
+ */
+s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const int32_t* selected,
+                                 int32_t k, float softmax_scale, s3r_dtype out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_dense_verify_attn: full-attention verification of the draft ("dense
+ * verification still requires the complete historical KV cache", S3R
+ * Abstract). Query i = 0..n_q-1 of sequence b sits at position
+ * seq_len - n_q + i and attends causally to every position <= its own, over
+ * all pages of the sequence. n_q = gamma + 1 (the last committed token plus
+ * the gamma drafts) gives the gamma + 1 target distributions of one round.
+ *   q    [B][n_q][Hq][D] kv dtype.
+ *   out  [B][n_q][Hq][D] in out_dtype.
+ * Errors: INVALID_ARGUMENT for NULL pointers or n_q < 1; UNSUPPORTED if
+ * G * n_q > 64; WORKSPACE_TOO_SMALL as above.
+ */
+s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t n_q,
+                                 float softmax_scale, s3r_dtype out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_spec_sample: exact speculative sampling of one round ("exact speculative
+ * sampling", S3R Abstract; the rule of the speculative decoding/sampling works
+ * its reference list cites). Per sequence b, with p_i = softmax(target_i / T)
+ * and q_i = softmax(draft_i / T):
+ *   for i = 0..gamma-1, x = draft_tokens[b][i], u = U(b, i, 0):
+ *     accept iff (q_i(x) > 0 and u < p_i(x)/q_i(x)) or (q_i(x) = 0 and p_i(x) > 0);
+ *     at the first reject emit ICDF(max(0, p_i - q_i), U(b, i, 1)) (p_i if that
+ *     residual has no mass) and stop;
+ *   if all accept, emit the bonus ICDF(p_gamma, U(b, gamma, 1)).
+ * ICDF(w, u) is the smallest token t with sum_{s<=t} w_s > u * sum(w).
+ * U(b, slot, stream) = (w0 >> 11) * 2^-53 with w0 word 0 of Philox4x64-10
+ * (Salmon et al., SC'11) at key (seed, 0), counter (offset, b, slot, stream).
+ *   draft_logits  [B][gamma][V] fp32;  target_logits [B][gamma+1][V] fp32.
+ *   draft_tokens  [B][gamma] int32 in [0, V).
+ *   out_tokens    out [B][gamma+1] int32: accepted drafts, then the drawn token,
+ *                 then -1.
+ *   num_accepted  out [B] int32: accepted drafts n (n + 1 tokens committed).
+ * Errors: INVALID_ARGUMENT for NULL pointers, num_seqs < 1, vocab < 1, gamma
+ * outside 1..16, temperature not finite and > 0; WORKSPACE_TOO_SMALL.
+ * Deterministic: no floating-point atomics; reductions run in a fixed order.
+ */
+s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                           const float* draft_logits, const float* target_logits,
+                           const int32_t* draft_tokens, float temperature, uint64_t seed,
+                           uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (host, never NULL). */
+const char* s3r_status_string(s3r_status status);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t s3r_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S3R_H */

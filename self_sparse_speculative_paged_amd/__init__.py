@@ -1,0 +1,201 @@
+"""Python binding of libs3r, the S3R hot path on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory and the current stream. Each function checks its
+tensors' device, dtype, shape and contiguity, passes raw pointers to the C ABI
+and raises S3RError on a non-zero status. Outputs and workspaces may be passed
+in (pre-allocated, e.g. for timing or graph capture) or are allocated here.
+
+Entry points (same names as include/s3r.h without the prefix):
+  page_bounds_update, page_select, sparse_draft_attn, dense_verify_attn,
+  spec_sample, and the workspace queries.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PagedKV
+
+__all__ = [
+    "S3RError", "PagedKVCache", "page_bounds_update", "page_select", "sparse_draft_attn",
+    "dense_verify_attn", "spec_sample", "page_select_workspace", "attn_workspace",
+    "spec_sample_workspace", "version",
+]
+
+_KV_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
+
+
+class S3RError(RuntimeError):
+    def __init__(self, status, where):
+        lib = _lib.load()
+        super().__init__(f"{where}: {lib.s3r_status_string(status).decode()} ({status})")
+        self.status = status
+
+
+def _check(status, where):
+    if status != _lib.S3R_OK:
+        raise S3RError(status, where)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class PagedKVCache:
+    """Caller-owned paged KV buffers plus the s3r_paged_kv struct describing them.
+
+    k_pool [N][Hkv][P][D], v_pool [N][Hkv][D][P] (value transposed per page),
+    page_table [B][max_pages] int32, seq_lens [B] int32 (device tensors).
+    """
+
+    def __init__(self, k_pool, v_pool, page_table, seq_lens, num_q_heads, total_pages_hint=0):
+        if k_pool.dtype not in _KV_DTYPES:
+            raise ValueError(f"kv dtype must be float32 or bfloat16, got {k_pool.dtype}")
+        n_phys, hkv, P, D = k_pool.shape
+        _dev(k_pool, "k_pool")
+        _dev(v_pool, "v_pool", k_pool.dtype, (n_phys, hkv, D, P))
+        B, maxp = page_table.shape
+        _dev(page_table, "page_table", torch.int32)
+        self.k_pool, self.v_pool, self.page_table = k_pool, v_pool, page_table
+        self.num_q_heads = num_q_heads
+        self.total_pages_hint = int(total_pages_hint)
+        self.dtype = k_pool.dtype
+        self.B, self.Hkv, self.P, self.D, self.max_pages = B, hkv, P, D, maxp
+        self.set_seq_lens(seq_lens)
+
+    def set_seq_lens(self, seq_lens):
+        _dev(seq_lens, "seq_lens", torch.int32, (self.B,))
+        self.seq_lens = seq_lens
+        self.struct = PagedKV(
+            self.B, self.num_q_heads, self.Hkv, self.D, self.P, self.max_pages,
+            self.total_pages_hint, _KV_DTYPES[self.dtype], self.k_pool.data_ptr(),
+            self.v_pool.data_ptr(), self.page_table.data_ptr(), seq_lens.data_ptr())
+        return self
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def version():
+    return _lib.load().s3r_version()
+
+
+def page_select_workspace(kv, budget_tokens):
+    return _lib.load().s3r_page_select_workspace(kv.ref(), budget_tokens)
+
+
+def attn_workspace(kv, n_queries, max_pages_attended):
+    return _lib.load().s3r_attn_workspace(kv.ref(), n_queries, max_pages_attended)
+
+
+def spec_sample_workspace(num_seqs, gamma, vocab):
+    return _lib.load().s3r_spec_sample_workspace(num_seqs, gamma, vocab)
+
+
+def _workspace(nbytes, like, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+    _dev(workspace, "workspace", torch.uint8)
+    return workspace
+
+
+def page_bounds_update(kv, bounds, first_pos=None, max_pages_touched=1, stream=None):
+    """Recompute the key min/max bounds of touched pages (all pages if first_pos is None)."""
+    lib = _lib.load()
+    n_phys = kv.k_pool.shape[0]
+    b = _dev(bounds, "bounds", kv.dtype, (n_phys, kv.Hkv, 2, kv.D))
+    fp = None if first_pos is None else _dev(first_pos, "first_pos", torch.int32, (kv.B,))
+    _check(lib.s3r_page_bounds_update(kv.ref(), b, fp, int(max_pages_touched), _stream(stream)),
+           "s3r_page_bounds_update")
+    return bounds
+
+
+def page_select(kv, bounds, q, budget_tokens, scale, selected=None, num_selected=None,
+                workspace=None, stream=None):
+    """Top-k pages per (sequence, kv head) by key-bound score; returns (selected, num_selected)."""
+    lib = _lib.load()
+    k = budget_tokens // kv.P
+    if selected is None:
+        selected = torch.empty((kv.B, kv.Hkv, k), dtype=torch.int32, device=q.device)
+    if num_selected is None:
+        num_selected = torch.empty((kv.B,), dtype=torch.int32, device=q.device)
+    ws = _workspace(page_select_workspace(kv, budget_tokens), q, workspace)
+    n_phys = kv.k_pool.shape[0]
+    _check(lib.s3r_page_select(
+        kv.ref(), _dev(bounds, "bounds", kv.dtype, (n_phys, kv.Hkv, 2, kv.D)),
+        _dev(q, "q", kv.dtype, (kv.B, kv.num_q_heads, kv.D)), int(budget_tokens), float(scale),
+        _dev(selected, "selected", torch.int32, (kv.B, kv.Hkv, k)),
+        _dev(num_selected, "num_selected", torch.int32, (kv.B,)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)), "s3r_page_select")
+    return selected, num_selected
+
+
+_OUT_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
+
+
+def sparse_draft_attn(kv, q, selected, scale, out=None, out_dtype=torch.float32,
+                      workspace=None, stream=None):
+    """One draft step's attention over the selected pages; returns out [B][Hq][D]."""
+    lib = _lib.load()
+    k = selected.shape[-1]
+    if out is None:
+        out = torch.empty((kv.B, kv.num_q_heads, kv.D), dtype=out_dtype, device=q.device)
+    ws = _workspace(attn_workspace(kv, 1, k), q, workspace)
+    _check(lib.s3r_sparse_draft_attn(
+        kv.ref(), _dev(q, "q", kv.dtype, (kv.B, kv.num_q_heads, kv.D)),
+        _dev(selected, "selected", torch.int32, (kv.B, kv.Hkv, k)), k, float(scale),
+        _OUT_DTYPES[out.dtype], _dev(out, "out", None, (kv.B, kv.num_q_heads, kv.D)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)), "s3r_sparse_draft_attn")
+    return out
+
+
+def dense_verify_attn(kv, q, scale, out=None, out_dtype=torch.float32, workspace=None,
+                      stream=None):
+    """Causal verify attention of q [B][n_q][Hq][D] over every page; returns out like q."""
+    lib = _lib.load()
+    nq = q.shape[1]
+    shape = (kv.B, nq, kv.num_q_heads, kv.D)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=q.device)
+    ws = _workspace(attn_workspace(kv, nq, kv.max_pages), q, workspace)
+    _check(lib.s3r_dense_verify_attn(
+        kv.ref(), _dev(q, "q", kv.dtype, shape), nq, float(scale), _OUT_DTYPES[out.dtype],
+        _dev(out, "out", None, shape), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+        _stream(stream)), "s3r_dense_verify_attn")
+    return out
+
+
+def spec_sample(draft_logits, target_logits, draft_tokens, temperature, seed, offset,
+                out_tokens=None, num_accepted=None, workspace=None, stream=None):
+    """Exact speculative sampling of one round; returns (out_tokens, num_accepted)."""
+    lib = _lib.load()
+    B, gamma, V = draft_logits.shape
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=draft_logits.device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=draft_logits.device)
+    ws = _workspace(spec_sample_workspace(B, gamma, V), draft_logits, workspace)
+    _check(lib.s3r_spec_sample(
+        B, gamma, V, _dev(draft_logits, "draft_logits", torch.float32),
+        _dev(target_logits, "target_logits", torch.float32, (B, gamma + 1, V)),
+        _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma)), float(temperature),
+        int(seed), int(offset), _dev(out_tokens, "out_tokens", torch.int32, (B, gamma + 1)),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)), "s3r_spec_sample")
+    return out_tokens, num_accepted

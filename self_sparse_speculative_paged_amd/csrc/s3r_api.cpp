@@ -1,0 +1,204 @@
+// C ABI of libs3r: host-side validation (before any HIP call), workspace
+// sizing and kernel dispatch on the caller's stream. See include/s3r.h for the
+// contract of each entry point.
+#include <math.h>
+
+#include "s3r.h"
+#include "s3r_internal.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kMaxRows = 64;   // G * n_queries per kv head (4 MFMA row blocks)
+constexpr int32_t kMaxGamma = 16;
+
+s3r_status check_kv(const s3r_paged_kv* kv) {
+  if (kv == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (kv->num_seqs < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1 ||
+      kv->total_pages_hint < 0)
+    return S3R_ERR_INVALID_ARGUMENT;
+  if (kv->num_q_heads % kv->num_kv_heads != 0) return S3R_ERR_INVALID_ARGUMENT;
+  if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->page_table == nullptr || kv->seq_lens == nullptr)
+    return S3R_ERR_INVALID_ARGUMENT;
+  if (kv->kv_dtype != S3R_F32 && kv->kv_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return S3R_ERR_UNSUPPORTED;
+  if (kv->page_size != 16) return S3R_ERR_UNSUPPORTED;
+  if (kv->num_q_heads / kv->num_kv_heads > 8) return S3R_ERR_UNSUPPORTED;
+  return S3R_OK;
+}
+
+s3r_status check_workspace(void* ws, size_t have, size_t need) {
+  if (have < need) return S3R_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && ws == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  return S3R_OK;
+}
+
+s3r_status from_hip(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
+
+s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* sel, int32_t ksel,
+                         int32_t n_q, float scale, s3r_dtype out_dtype, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (s3r_status s = check_kv(kv)) return s;
+  if (q == nullptr || out == nullptr || n_q < 1 || !isfinite(scale)) return S3R_ERR_INVALID_ARGUMENT;
+  if (out_dtype != S3R_F32 && out_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  const int32_t G = kv->num_q_heads / kv->num_kv_heads;
+  if ((int64_t)G * n_q > kMaxRows) return S3R_ERR_UNSUPPORTED;
+  const int32_t max_items = sel ? ksel : kv->max_pages_per_seq;
+  const s3r::SplitPlan plan = s3r::plan_attention(*kv, n_q, max_items);
+  if (s3r_status s = check_workspace(ws, ws_bytes, plan.workspace_bytes)) return s;
+  s3r::AttnArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.q = q;
+  a.sel = sel;
+  a.out = out;
+  const size_t items = (size_t)kv->num_seqs * kv->num_kv_heads * plan.n_splits;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = a.part_o + items * plan.rows * kv->head_dim;
+  a.B = kv->num_seqs;
+  a.Hq = kv->num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = G;
+  a.D = kv->head_dim;
+  a.max_pages = kv->max_pages_per_seq;
+  a.nq = n_q;
+  a.ksel = ksel;
+  a.rows = plan.rows;
+  a.pages_per_split = plan.pages_per_split;
+  a.n_splits = plan.n_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_bf16 = out_dtype == S3R_BF16;
+  return from_hip(s3r::launch_attention(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t s3r_page_select_workspace(const s3r_paged_kv* kv, int32_t budget_tokens) {
+  (void)budget_tokens;
+  if (check_kv(kv) != S3R_OK) return 0;
+  return s3r::select_workspace_bytes(kv->num_seqs, kv->num_kv_heads, kv->max_pages_per_seq);
+}
+
+size_t s3r_attn_workspace(const s3r_paged_kv* kv, int32_t n_queries, int32_t max_pages_attended) {
+  if (check_kv(kv) != S3R_OK || n_queries < 1 || max_pages_attended < 1) return 0;
+  return s3r::plan_attention(*kv, n_queries, max_pages_attended).workspace_bytes;
+}
+
+size_t s3r_spec_sample_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab) {
+  if (num_seqs < 1 || gamma < 1 || gamma > kMaxGamma || vocab < 1) return 0;
+  return s3r::sample_workspace_bytes(num_seqs, gamma, vocab);
+}
+
+s3r_status s3r_page_bounds_update(const s3r_paged_kv* kv, void* bounds, const int32_t* first_pos,
+                                  int32_t max_pages_touched, void* stream) {
+  if (s3r_status s = check_kv(kv)) return s;
+  if (bounds == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (first_pos != nullptr && max_pages_touched < 1) return S3R_ERR_INVALID_ARGUMENT;
+  s3r::BoundsArgs a{};
+  a.k_pool = kv->k_pool;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.first_pos = first_pos;
+  a.bounds = bounds;
+  a.B = kv->num_seqs;
+  a.Hkv = kv->num_kv_heads;
+  a.D = kv->head_dim;
+  a.max_pages = kv->max_pages_per_seq;
+  a.pages_y = first_pos ? (max_pages_touched < kv->max_pages_per_seq ? max_pages_touched
+                                                                     : kv->max_pages_per_seq)
+                        : kv->max_pages_per_seq;
+  return from_hip(s3r::launch_bounds(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+s3r_status s3r_page_select(const s3r_paged_kv* kv, const void* bounds, const void* q,
+                           int32_t budget_tokens, float softmax_scale, int32_t* selected,
+                           int32_t* num_selected, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (s3r_status s = check_kv(kv)) return s;
+  if (bounds == nullptr || q == nullptr || selected == nullptr || num_selected == nullptr)
+    return S3R_ERR_INVALID_ARGUMENT;
+  if (budget_tokens < kv->page_size || !isfinite(softmax_scale)) return S3R_ERR_INVALID_ARGUMENT;
+  if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
+  const size_t need = s3r::select_workspace_bytes(kv->num_seqs, kv->num_kv_heads, kv->max_pages_per_seq);
+  if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  s3r::SelectArgs a{};
+  a.bounds = bounds;
+  a.q = q;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.scores = static_cast<float*>(workspace);
+  a.selected = selected;
+  a.num_selected = num_selected;
+  a.B = kv->num_seqs;
+  a.Hq = kv->num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = kv->num_q_heads / kv->num_kv_heads;
+  a.D = kv->head_dim;
+  a.max_pages = kv->max_pages_per_seq;
+  a.k = budget_tokens / kv->page_size;
+  a.scale = softmax_scale;
+  return from_hip(s3r::launch_select(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const int32_t* selected,
+                                 int32_t k, float softmax_scale, s3r_dtype out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (selected == nullptr || k < 1) return S3R_ERR_INVALID_ARGUMENT;
+  return run_attention(kv, q, selected, k, 1, softmax_scale, out_dtype, out, workspace,
+                       workspace_bytes, stream);
+}
+
+s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t n_q,
+                                 float softmax_scale, s3r_dtype out_dtype, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(kv, q, nullptr, 0, n_q, softmax_scale, out_dtype, out, workspace,
+                       workspace_bytes, stream);
+}
+
+s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                           const float* draft_logits, const float* target_logits,
+                           const int32_t* draft_tokens, float temperature, uint64_t seed,
+                           uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 1 || vocab < 1 || gamma < 1 || gamma > kMaxGamma) return S3R_ERR_INVALID_ARGUMENT;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARGUMENT;
+  if (draft_logits == nullptr || target_logits == nullptr || draft_tokens == nullptr ||
+      out_tokens == nullptr || num_accepted == nullptr)
+    return S3R_ERR_INVALID_ARGUMENT;
+  const size_t need = s3r::sample_workspace_bytes(num_seqs, gamma, vocab);
+  if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  s3r::SampleArgs a{};
+  a.draft_logits = draft_logits;
+  a.target_logits = target_logits;
+  a.draft_tokens = draft_tokens;
+  a.out_tokens = out_tokens;
+  a.num_accepted = num_accepted;
+  a.workspace = workspace;
+  a.B = num_seqs;
+  a.gamma = gamma;
+  a.V = vocab;
+  a.n_chunks = s3r::sample_chunks(vocab);
+  a.temperature = temperature;
+  a.seed = seed;
+  a.offset = offset;
+  return from_hip(s3r::launch_sample(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* s3r_status_string(s3r_status status) {
+  switch (status) {
+    case S3R_OK: return "S3R_OK";
+    case S3R_ERR_INVALID_ARGUMENT: return "S3R_ERR_INVALID_ARGUMENT";
+    case S3R_ERR_UNSUPPORTED: return "S3R_ERR_UNSUPPORTED";
+    case S3R_ERR_WORKSPACE_TOO_SMALL: return "S3R_ERR_WORKSPACE_TOO_SMALL";
+    case S3R_ERR_HIP: return "S3R_ERR_HIP";
+    default: return "S3R_ERR_UNKNOWN";
+  }
+}
+
+int32_t s3r_version(void) { return kVersion; }
+
+}  // extern "C"

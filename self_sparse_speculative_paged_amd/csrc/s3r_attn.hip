@@ -1,0 +1,475 @@
+// Paged GQA attention for the sparse draft and the dense verify.
+//
+// "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
+// Abstract: the draft attends sparsely, the verify attends to the complete KV
+// history; draft and verify share parameters and therefore one KV cache. Both
+// are softmax(scale * q K^T) V over a token set; they differ only in which
+// pages are read (a selection row vs every page) and in the number of query
+// positions (1 vs gamma + 1, causally masked).
+//
+// One wave64 workgroup owns one (sequence, kv head, split) work item and all
+// rows = G * n_queries query rows of that kv head, so every K/V tile read from
+// HBM is used by the whole GQA group and all verify positions.
+//
+// bf16 path, per window of two pages (32 tokens), on MFMA 16x16x32 bf16:
+//   S^T[token][row] = K[token][:] . Q[row][:]     A = K rows,  B = Q^T
+//   O^T[d][row]    += V^T[d][token] P^T[token][row]  A = V^T,  B = P^T
+// With the row index on the lane-within-16 axis of both products, a lane owns
+// one query row in S^T, P^T and O^T alike: the softmax state is lane-local and
+// a row maximum needs only two cross-lane steps. V is stored transposed inside
+// each page ([D][P]) so the A operand of O^T (8 consecutive tokens of one d) is
+// one 16-byte load. P is split into bf16 hi + lo parts so the P.V product keeps
+// ~16 mantissa bits. The fp32 path does the same on MFMA 16x16x4 f32, one page
+// per window.
+#include "s3r_common.h"
+#include "s3r_internal.h"
+
+namespace s3r {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Resolves the two logical pages of a window to physical pages. Invalid pages
+// (past the range, -1 in a selection, or past the sequence) alias a valid page
+// so every load stays in bounds; their tokens are masked.
+struct WindowPages {
+  int lpA, lpB;      // logical page ids, -1 when invalid
+  int physA, physB;
+};
+
+template <bool kSparse>
+__device__ __forceinline__ int logical_page(const int32_t* sel, int idx, int n_pages) {
+  int lp = kSparse ? sel[idx] : idx;
+  return (lp >= 0 && lp < n_pages) ? lp : -1;
+}
+
+// Online-softmax update of one 16-row block for one window. x[] holds this
+// lane's logits (log2 units) for its row; returns p = 2^(x - m_new) in x.
+template <int kTpl>
+__device__ __forceinline__ float softmax_update(float (&x)[kTpl], float& m_run, float& l_run) {
+  float mloc = x[0];
+#pragma unroll
+  for (int e = 1; e < kTpl; ++e) mloc = fmaxf(mloc, x[e]);
+  mloc = wave_xor_max<16, 32>(mloc);
+  const float m_new = fmaxf(m_run, mloc);
+  const float msafe = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - msafe);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < kTpl; ++e) {
+    x[e] = __builtin_amdgcn_exp2f(x[e] - msafe);
+    s += x[e];
+  }
+  l_run = l_run * alpha + s;
+  m_run = m_new;
+  return alpha;
+}
+
+template <int kD, int kNB>
+__device__ __forceinline__ void write_partial(const AttnArgs& a, int b, int h, int split,
+                                              const float (&m_run)[kNB], float (&l_run)[kNB],
+                                              const f32x4 (&acc)[kNB][kD / 16]) {
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const size_t item = ((size_t)b * a.Hkv + h) * a.n_splits + split;
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const float l = wave_xor_sum<16, 32>(l_run[nb]);
+    const int row = 16 * nb + l16;
+    if (row < a.rows) {
+      if (g4 == 0) {
+        a.part_ml[(item * a.rows + row) * 2 + 0] = m_run[nb];
+        a.part_ml[(item * a.rows + row) * 2 + 1] = l;
+      }
+      float* o = a.part_o + (item * a.rows + row) * kD + 4 * g4;
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb) *reinterpret_cast<f32x4*>(o + 16 * mb) = acc[nb][mb];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 KV
+// ---------------------------------------------------------------------------
+template <int kD, int kNB>
+struct Bf16Tile {
+  bf16x8 k[2][kD / 32];  // A operand of S^T for the two 16-token M-blocks
+  bf16x8 v[kD / 16];     // A operand of O^T for each 16-wide d block
+};
+
+template <int kD, int kNB>
+__device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint16_t* kp,
+                                               const uint16_t* vp, int Hkv, int h,
+                                               const WindowPages& w) {
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  // M-block mb, row m = l16 holds window token 8*(m/4) + 4*mb + m%4: tokens
+  // 0..15 come from page A (l16 < 8), 16..31 from page B.
+  const int kphys = (l16 >= 8) ? w.physB : w.physA;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int slot = (8 * (l16 >> 2) + 4 * mb + (l16 & 3)) & 15;
+    const uint16_t* base =
+        kp + (((size_t)kphys * Hkv + h) * kPage + slot) * kD + (kD / 4) * g4;
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s) t.k[mb][s] = *reinterpret_cast<const bf16x8*>(base + 8 * s);
+  }
+  // O^T A operand: lane holds V^T[d = 16*mb + l16][window tokens 8*g4 .. 8*g4+7].
+  const int vphys = (g4 >= 2) ? w.physB : w.physA;
+  const uint16_t* vbase = vp + ((size_t)vphys * Hkv + h) * kD * kPage + l16 * kPage + 8 * (g4 & 1);
+#pragma unroll
+  for (int mb = 0; mb < kD / 16; ++mb)
+    t.v[mb] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)16 * mb * kPage);
+}
+
+template <int kD, int kNB>
+__device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
+                                                  const bf16x8 (&qb)[kNB][kD / 32],
+                                                  const int (&qpos)[kNB], const WindowPages& w,
+                                                  bool need_mask, float scale_log2,
+                                                  float (&m_run)[kNB], float (&l_run)[kNB],
+                                                  f32x4 (&acc)[kNB][kD / 16]) {
+  const int lane = threadIdx.x, g4 = lane >> 4;
+  f32x4 sacc[2][kNB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      sacc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kD / 32; ++s)
+        sacc[mb][nb] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[mb][s], qb[nb][s], sacc[mb][nb], 0, 0, 0);
+    }
+  // This lane's tokens: window token 8*g4 + e, e = 4*mb + i.
+  const int lp = (g4 >= 2) ? w.lpB : w.lpA;
+  const int pos0 = 16 * lp + 8 * (g4 & 1);
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    float x[8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * mb + i] = sacc[mb][nb][i] * scale_log2;
+    if (need_mask) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (lp < 0 || pos0 + e > qpos[nb]) x[e] = kNegInf;
+    }
+    const float alpha = softmax_update<8>(x, m_run[nb], l_run[nb]);
+    if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb) acc[nb][mb] *= alpha;
+    }
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 hi = static_cast<__bf16>(x[e]);
+      phi[e] = hi;
+      plo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hi));
+    }
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb) {
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.v[mb], phi, acc[nb][mb], 0, 0, 0);
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.v[mb], plo, acc[nb][mb], 0, 0, 0);
+    }
+  }
+}
+
+template <int kD, int kNB, bool kSparse>
+__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x % a.n_splits;
+  const int bh = blockIdx.x / a.n_splits;
+  const int h = bh % a.Hkv, b = bh / a.Hkv;
+  const int seq_len = a.seq_lens[b];
+  const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
+  const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
+  const int j0 = split * a.pages_per_split;
+  if (j0 >= n_items) return;
+  const int j1 = min(j0 + a.pages_per_split, n_items);
+
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  const int32_t* sel = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+
+  bf16x8 qb[kNB][kD / 32];
+  int qpos[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int row = 16 * nb + l16;
+    if (row < a.rows) {
+      const int gl = row / a.nq, i = row % a.nq;
+      const uint16_t* qrow =
+          qg + (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + (kD / 4) * g4;
+#pragma unroll
+      for (int s = 0; s < kD / 32; ++s) qb[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
+      qpos[nb] = seq_len - a.nq + i;
+    } else {
+#pragma unroll
+      for (int s = 0; s < kD / 32; ++s) qb[nb][s] = bf16x8{};
+      qpos[nb] = -1;
+    }
+  }
+
+  float m_run[kNB], l_run[kNB];
+  f32x4 acc[kNB][kD / 16];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int min_qpos = seq_len - a.nq;
+  const int fallback = pt[0];
+  auto pages_of = [&](int jj) {
+    WindowPages w;
+    w.lpA = logical_page<kSparse>(sel, jj, n_pages);
+    w.lpB = (jj + 1 < j1) ? logical_page<kSparse>(sel, jj + 1, n_pages) : -1;
+    w.physA = w.lpA >= 0 ? pt[w.lpA] : fallback;
+    w.physB = w.lpB >= 0 ? pt[w.lpB] : w.physA;
+    return w;
+  };
+  auto masked = [&](const WindowPages& w) {
+    return w.lpA < 0 || w.lpB < 0 || 16 * max(w.lpA, w.lpB) + 15 > min_qpos;
+  };
+
+  // Two tiles in flight: the loads of window n+1 are issued before window n is
+  // computed.
+  Bf16Tile<kD, kNB> t0, t1;
+  WindowPages w0 = pages_of(j0), w1;
+  load_bf16_tile<kD, kNB>(t0, kp, vp, a.Hkv, h, w0);
+  for (int jj = j0; jj < j1; jj += 4) {
+    const bool has1 = jj + 2 < j1;
+    if (has1) {
+      w1 = pages_of(jj + 2);
+      load_bf16_tile<kD, kNB>(t1, kp, vp, a.Hkv, h, w1);
+    }
+    compute_bf16_tile<kD, kNB>(t0, qb, qpos, w0, masked(w0), a.scale_log2, m_run, l_run, acc);
+    if (!has1) break;
+    const bool has0 = jj + 4 < j1;
+    if (has0) {
+      w0 = pages_of(jj + 4);
+      load_bf16_tile<kD, kNB>(t0, kp, vp, a.Hkv, h, w0);
+    }
+    compute_bf16_tile<kD, kNB>(t1, qb, qpos, w1, masked(w1), a.scale_log2, m_run, l_run, acc);
+  }
+  write_partial<kD, kNB>(a, b, h, split, m_run, l_run, acc);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 KV: one page (16 tokens) per window on MFMA 16x16x4 f32.
+// ---------------------------------------------------------------------------
+template <int kD>
+struct F32Tile {
+  float k[kD / 4];  // K[slot l16][d = (D/4)*g4 + s]
+  f32x4 v[kD / 16]; // V^T[d = 16*mb + l16][slots 4*g4 .. 4*g4+3]
+};
+
+template <int kD>
+__device__ __forceinline__ void load_f32_tile(F32Tile<kD>& t, const float* kp, const float* vp,
+                                              int Hkv, int h, int phys) {
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const float* kb = kp + (((size_t)phys * Hkv + h) * kPage + l16) * kD + (kD / 4) * g4;
+#pragma unroll
+  for (int s = 0; s < kD / 16; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(kb + 4 * s);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t.k[4 * s + e] = v[e];
+  }
+  const float* vb = vp + ((size_t)phys * Hkv + h) * kD * kPage + l16 * kPage + 4 * g4;
+#pragma unroll
+  for (int mb = 0; mb < kD / 16; ++mb)
+    t.v[mb] = *reinterpret_cast<const f32x4*>(vb + (size_t)16 * mb * kPage);
+}
+
+template <int kD, int kNB, bool kSparse>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x % a.n_splits;
+  const int bh = blockIdx.x / a.n_splits;
+  const int h = bh % a.Hkv, b = bh / a.Hkv;
+  const int seq_len = a.seq_lens[b];
+  const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
+  const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
+  const int j0 = split * a.pages_per_split;
+  if (j0 >= n_items) return;
+  const int j1 = min(j0 + a.pages_per_split, n_items);
+
+  const float* kp = static_cast<const float*>(a.k_pool);
+  const float* vp = static_cast<const float*>(a.v_pool);
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  const int32_t* sel = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
+  const float* qg = static_cast<const float*>(a.q);
+
+  float qb[kNB][kD / 4];
+  int qpos[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int row = 16 * nb + l16;
+    if (row < a.rows) {
+      const int gl = row / a.nq, i = row % a.nq;
+      const float* qrow = qg + (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + (kD / 4) * g4;
+#pragma unroll
+      for (int s = 0; s < kD / 4; ++s) qb[nb][s] = qrow[s];
+      qpos[nb] = seq_len - a.nq + i;
+    } else {
+#pragma unroll
+      for (int s = 0; s < kD / 4; ++s) qb[nb][s] = 0.f;
+      qpos[nb] = -1;
+    }
+  }
+  float m_run[kNB], l_run[kNB];
+  f32x4 acc[kNB][kD / 16];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int min_qpos = seq_len - a.nq;
+  const int fallback = pt[0];
+  F32Tile<kD> t;
+  for (int jj = j0; jj < j1; ++jj) {
+    const int lp = logical_page<kSparse>(sel, jj, n_pages);
+    load_f32_tile<kD>(t, kp, vp, a.Hkv, h, lp >= 0 ? pt[lp] : fallback);
+    const bool need_mask = lp < 0 || 16 * lp + 15 > min_qpos;
+    f32x4 sacc[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      sacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kD / 4; ++s)
+        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[s], qb[nb][s], sacc[nb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = sacc[nb][i] * a.scale_log2;
+        if (need_mask && (lp < 0 || 16 * lp + 4 * g4 + i > qpos[nb])) x[i] = kNegInf;
+      }
+      const float alpha = softmax_update<4>(x, m_run[nb], l_run[nb]);
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int mb = 0; mb < kD / 16; ++mb) acc[nb][mb] *= alpha;
+      }
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[mb][i], x[i], acc[nb][mb], 0, 0, 0);
+    }
+  }
+  write_partial<kD, kNB>(a, b, h, split, m_run, l_run, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV combine: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// One wave per (sequence, query, q head) output row.
+// ---------------------------------------------------------------------------
+template <int kD, bool kSparse>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % a.Hq;
+  const int t = blockIdx.x / a.Hq;
+  const int i = t % a.nq, b = t / a.nq;
+  const int h = g / a.G, row = (g % a.G) * a.nq + i;
+  const int seq_len = a.seq_lens[b];
+  const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
+  const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
+  const int ns = (n_items + a.pages_per_split - 1) / a.pages_per_split;
+  const size_t item0 = ((size_t)b * a.Hkv + h) * a.n_splits;
+
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((item0 + s) * a.rows + row) * 2]);
+  float o[kD / 64] = {};
+  float den = 0.f;
+  if (M != kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const size_t r = (item0 + s) * a.rows + row;
+      const float w = __builtin_amdgcn_exp2f(a.part_ml[r * 2] - M);
+      den += w * a.part_ml[r * 2 + 1];
+#pragma unroll
+      for (int e = 0; e < kD / 64; ++e) o[e] += w * a.part_o[r * kD + lane + 64 * e];
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const size_t obase = (((size_t)b * a.nq + i) * a.Hq + g) * kD;
+#pragma unroll
+  for (int e = 0; e < kD / 64; ++e) {
+    const float v = o[e] * inv;
+    if (a.out_bf16)
+      static_cast<uint16_t*>(a.out)[obase + lane + 64 * e] = f32_to_bf16_bits(v);
+    else
+      static_cast<float*>(a.out)[obase + lane + 64 * e] = v;
+  }
+}
+
+template <int kD, int kNB, bool kSparse>
+hipError_t launch_typed(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_splits));
+  if (dt == S3R_BF16)
+    hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<kD, kNB, kSparse>), grid, dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<kD, kSparse>), dim3((unsigned)((size_t)a.B * a.nq * a.Hq)),
+                     dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int kD, bool kSparse>
+hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
+  switch ((a.rows + 15) / 16) {
+    case 1: return launch_typed<kD, 1, kSparse>(a, dt, stream);
+    case 2: return launch_typed<kD, 2, kSparse>(a, dt, stream);
+    case 3: return launch_typed<kD, 3, kSparse>(a, dt, stream);
+    case 4: return launch_typed<kD, 4, kSparse>(a, dt, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items) {
+  // Aim for ~8 resident waves on each of the 256 CUs.
+  constexpr long kTargetItems = 2048;
+  constexpr long kMinPagesPerSplit = 16;
+  SplitPlan p{};
+  const long B = kv.num_seqs, Hkv = kv.num_kv_heads;
+  const int G = kv.num_q_heads / kv.num_kv_heads;
+  p.rows = G * n_queries;
+  p.row_blocks = (p.rows + 15) / 16;
+  long total = (long)B * max_items;
+  if (kv.total_pages_hint > 0 && kv.total_pages_hint < total) total = kv.total_pages_hint;
+  const double avg = (double)total / (double)B;
+  long want = (kTargetItems + B * Hkv - 1) / (B * Hkv);
+  if (want < 1) want = 1;
+  long pps = (long)((avg + want - 1) / want);
+  if (pps < kMinPagesPerSplit) pps = kMinPagesPerSplit;
+  pps = (pps + 1) & ~1L;
+  const long cap = ((long)max_items + 1) & ~1L;
+  if (pps > cap) pps = cap;
+  p.pages_per_split = (int32_t)pps;
+  p.n_splits = (int32_t)((max_items + pps - 1) / pps);
+  const size_t items = (size_t)B * Hkv * p.n_splits;
+  p.workspace_bytes = items * p.rows * ((size_t)kv.head_dim + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream) {
+  const bool sparse = a.sel != nullptr;
+  if (a.D == 128)
+    return sparse ? launch_nb<128, true>(a, kv_dtype, stream) : launch_nb<128, false>(a, kv_dtype, stream);
+  if (a.D == 64)
+    return sparse ? launch_nb<64, true>(a, kv_dtype, stream) : launch_nb<64, false>(a, kv_dtype, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace s3r

@@ -1,0 +1,87 @@
+// Internal launch interface between the C-ABI layer (s3r_api.cpp) and the
+// kernels. Everything here is host-visible plain data; no torch types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "s3r.h"
+
+namespace s3r {
+
+// Split-KV partition of one attention call: the attended items (pages, or
+// entries of a selection row) of every (sequence, kv head) are cut into
+// n_splits ranges of pages_per_split items; each range is one wave's work.
+struct SplitPlan {
+  int32_t pages_per_split;
+  int32_t n_splits;
+  int32_t rows;       // G * n_queries attention rows per kv head
+  int32_t row_blocks; // ceil(rows / 16): MFMA N-blocks
+  size_t workspace_bytes;
+};
+
+SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items);
+
+struct AttnArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const void* q;          // [B][nq][Hq][D]
+  const int32_t* sel;     // [B][Hkv][ksel] or nullptr (dense)
+  void* out;              // [B][nq][Hq][D]
+  float* part_o;          // [items][rows][D]
+  float* part_ml;         // [items][rows][2] (running max in log2 units, sum)
+  int32_t B, Hq, Hkv, G, D, max_pages, nq, ksel;
+  int32_t rows, pages_per_split, n_splits;
+  float scale_log2;       // softmax_scale * log2(e)
+  int32_t out_bf16;
+};
+
+hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
+
+struct BoundsArgs {
+  const void* k_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* first_pos;  // nullptr = all pages
+  void* bounds;
+  int32_t B, Hkv, D, max_pages, pages_y;
+};
+
+hipError_t launch_bounds(const BoundsArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
+
+struct SelectArgs {
+  const void* bounds;
+  const void* q;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* scores;        // workspace [B][Hkv][max_pages]
+  int32_t* selected;    // [B][Hkv][k]
+  int32_t* num_selected;
+  int32_t B, Hq, Hkv, G, D, max_pages, k;
+  float scale;
+};
+
+hipError_t launch_select(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
+size_t select_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_pages);
+int32_t select_max_pages_supported();
+
+struct SampleArgs {
+  const float* draft_logits;
+  const float* target_logits;
+  const int32_t* draft_tokens;
+  int32_t* out_tokens;
+  int32_t* num_accepted;
+  void* workspace;
+  int32_t B, gamma, V, n_chunks;
+  float temperature;
+  uint64_t seed, offset;
+};
+
+int32_t sample_chunks(int32_t vocab);
+size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+
+}  // namespace s3r

@@ -1,0 +1,108 @@
+"""The C-ABI library loads and exports every symbol include/s3r.h declares, and
+every invalid argument is rejected on the host before any HIP call (no GPU is
+touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from self_sparse_speculative_paged_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "s3r.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(s3r_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.s3r_version() == 100
+    assert lib.s3r_status_string(3) == b"S3R_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.s3r_status_string(99) == b"S3R_ERR_UNKNOWN"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _kv(**kw):
+    f = dict(num_seqs=2, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+             max_pages_per_seq=8, total_pages_hint=0, kv_dtype=_lib.S3R_BF16,
+             k_pool=FAKE, v_pool=FAKE, page_table=FAKE, seq_lens=FAKE)
+    f.update(kw)
+    return _lib.PagedKV(**f)
+
+
+BAD_KV = [
+    (dict(num_seqs=0), 1), (dict(num_q_heads=3), 1), (dict(num_kv_heads=0), 1),
+    (dict(max_pages_per_seq=0), 1), (dict(total_pages_hint=-1), 1), (dict(k_pool=None), 1),
+    (dict(v_pool=None), 1), (dict(page_table=None), 1), (dict(seq_lens=None), 1),
+    (dict(head_dim=96), 2), (dict(page_size=32), 2), (dict(kv_dtype=7), 2),
+    (dict(num_q_heads=18, num_kv_heads=2), 2),
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_KV)
+def test_invalid_kv_rejected_everywhere(bad, code):
+    lib = _lib.load()
+    kv = ctypes.byref(_kv(**bad))
+    v = ctypes.c_void_p(FAKE)
+    assert lib.s3r_page_bounds_update(kv, v, None, 1, None) == code
+    assert lib.s3r_page_select(kv, v, v, 64, 0.1, v, v, v, 1 << 30, None) == code
+    assert lib.s3r_sparse_draft_attn(kv, v, v, 4, 0.1, 0, v, v, 1 << 30, None) == code
+    assert lib.s3r_dense_verify_attn(kv, v, 5, 0.1, 0, v, v, 1 << 30, None) == code
+    assert lib.s3r_attn_workspace(kv, 5, 8) == 0
+    assert lib.s3r_page_select_workspace(kv, 64) == 0
+
+
+def test_invalid_call_arguments():
+    lib = _lib.load()
+    kv = ctypes.byref(_kv())
+    v = ctypes.c_void_p(FAKE)
+    big = 1 << 30
+    assert lib.s3r_page_bounds_update(kv, None, None, 1, None) == 1
+    assert lib.s3r_page_bounds_update(kv, v, v, 0, None) == 1
+    assert lib.s3r_page_select(kv, v, v, 15, 0.1, v, v, v, big, None) == 1      # budget < P
+    assert lib.s3r_page_select(kv, None, v, 64, 0.1, v, v, v, big, None) == 1
+    assert lib.s3r_page_select(kv, v, v, 64, float("nan"), v, v, v, big, None) == 1
+    need = lib.s3r_page_select_workspace(kv, 64)
+    assert need == 2 * 2 * 8 * 4
+    assert lib.s3r_page_select(kv, v, v, 64, 0.1, v, v, v, need - 1, None) == 3
+    assert lib.s3r_page_select(kv, v, v, 64, 0.1, v, v, None, need, None) == 1
+    assert lib.s3r_sparse_draft_attn(kv, v, None, 4, 0.1, 0, v, v, big, None) == 1
+    assert lib.s3r_sparse_draft_attn(kv, v, v, 0, 0.1, 0, v, v, big, None) == 1
+    assert lib.s3r_sparse_draft_attn(kv, v, v, 4, 0.1, 5, v, v, big, None) == 2   # out dtype
+    assert lib.s3r_dense_verify_attn(kv, v, 0, 0.1, 0, v, v, big, None) == 1
+    assert lib.s3r_dense_verify_attn(kv, None, 5, 0.1, 0, v, v, big, None) == 1
+    assert lib.s3r_dense_verify_attn(kv, v, 33, 0.1, 0, v, v, big, None) == 2     # 2*33 rows > 64
+    wneed = lib.s3r_attn_workspace(kv, 5, 8)
+    assert wneed > 0
+    assert lib.s3r_dense_verify_attn(kv, v, 5, 0.1, 0, v, v, wneed - 1, None) == 3
+    s = lib.s3r_spec_sample
+    assert s(0, 4, 1024, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
+    assert s(2, 0, 1024, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
+    assert s(2, 17, 1024, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
+    assert s(2, 4, 0, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
+    assert s(2, 4, 1024, v, v, v, 0.0, 0, 0, v, v, v, big, None) == 1
+    assert s(2, 4, 1024, v, v, v, float("inf"), 0, 0, v, v, v, big, None) == 1
+    assert s(2, 4, 1024, None, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
+    sneed = lib.s3r_spec_sample_workspace(2, 4, 1024)
+    assert sneed > 0 and lib.s3r_spec_sample_workspace(2, 17, 1024) == 0
+    assert s(2, 4, 1024, v, v, v, 1.0, 0, 0, v, v, v, sneed - 1, None) == 3
+
+
+def test_split_plan_workspace_scales_with_hint():
+    lib = _lib.load()
+    full = lib.s3r_attn_workspace(ctypes.byref(_kv(max_pages_per_seq=4096, num_seqs=8)), 5, 4096)
+    hinted = lib.s3r_attn_workspace(
+        ctypes.byref(_kv(max_pages_per_seq=4096, num_seqs=8, total_pages_hint=8 * 600)), 5, 4096)
+    assert hinted >= full  # a smaller average length means shorter splits, more of them

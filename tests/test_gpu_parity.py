@@ -1,0 +1,283 @@
+"""GPU parity: every libs3r entry point against the fp64 CPU oracle on the same
+seeded inputs, through the C ABI.
+
+Tolerances: page ids bit-exact outside a 1e-4 score tie window; tokens and
+accepted lengths bit-exact outside a 1e-6 decision window; attention max-abs
+1e-2 for bf16 KV (fp32 accumulation) and norm-wise relative 1e-5 for fp32 KV.
+Sizes span several KV tiles, split-KV partitions and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import self_sparse_speculative_paged_amd as s3r
+from s3r_inputs import make_workload
+from tests.oracle_io import f64, i32
+from tests.parity import check_pages, check_tokens
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _cfg(kv="bf16", D=128, G=4, Hkv=2, gamma=4, budget=64, V=512, heavy=0):
+    return dict(B=None, Hq=G * Hkv, Hkv=Hkv, D=D, L=None, P=16, budget=budget, gamma=gamma, V=V,
+                kv_dtype=kv, draft_sd=2.0, noise_sd=0.7, temperature=1.0, heavy_pages=heavy)
+
+
+def _make(cfg, ctx, seed=0, with_logits=False):
+    cfg = dict(cfg, B=len(ctx))
+    wl = make_workload(cfg, device="cpu", seed=seed, ctx=ctx, with_logits=with_logits)
+    for name in ("k_pool", "v_pool", "page_table", "q_verify", "draft_logits", "target_logits",
+                 "draft_tokens"):
+        t = getattr(wl, name)
+        if t is not None:
+            setattr(wl, name, t.to(DEV))
+    wl.seq_lens = [s.to(DEV) for s in wl.seq_lens]
+    return wl
+
+
+def _kv(wl, step, hint=0):
+    return s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[step],
+                            wl.cfg["Hq"], total_pages_hint=hint)
+
+
+def _check_attn(got, ref, kv):
+    got = got.float().cpu().numpy().astype(np.float64)
+    if kv == "f32":
+        err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-5, err
+    else:
+        err = np.max(np.abs(got - ref))
+        assert err <= 1e-2, err
+    return err
+
+
+VERIFY_CASES = [
+    # kv, D, G, Hkv, gamma, ctx
+    ("f32", 64, 2, 2, 4, (512, 300)),            # the tiny fp32 shape, ragged second sequence
+    ("f32", 128, 4, 2, 6, (250, 17)),
+    ("bf16", 128, 2, 2, 4, (700, 33, 1)),        # 10 rows: one MFMA row block
+    ("bf16", 128, 4, 2, 6, (1000, 515, 129)),    # 28 rows: two row blocks (Qwen3-8B heads)
+    ("bf16", 128, 4, 2, 8, (777, 64)),           # 36 rows: three row blocks
+    ("bf16", 64, 8, 1, 7, (400, 95)),            # 64 rows: four row blocks, D=64
+    ("bf16", 64, 2, 3, 3, (48, 2049)),
+]
+
+
+@pytest.mark.parametrize("kv,D,G,Hkv,gamma,ctx", VERIFY_CASES)
+def test_dense_verify_matches_oracle(kv, D, G, Hkv, gamma, ctx):
+    wl = _make(_cfg(kv, D, G, Hkv, gamma), list(ctx), seed=len(ctx) + D + G)
+    scale = 1.0 / np.sqrt(D)
+    kvc = _kv(wl, gamma)
+    out = s3r.dense_verify_attn(kvc, wl.q_verify, scale)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify_attn(f64(wl.q_verify), f64(wl.k_pool), f64(wl.v_pool),
+                                   i32(wl.page_table), i32(wl.seq_lens[gamma]), scale)
+    _check_attn(out, ref, kv)
+    if kv == "bf16":  # bf16 output: the tolerance plus the output's own rounding
+        outb = s3r.dense_verify_attn(kvc, wl.q_verify, scale, out_dtype=torch.bfloat16)
+        got = outb.float().cpu().numpy()
+        assert np.all(np.abs(got - ref) <= 1e-2 + np.abs(ref) * 2.0**-8)
+
+
+@pytest.mark.parametrize("kv,D", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_page_bounds_exact(kv, D):
+    wl = _make(_cfg(kv, D), [300, 17, 48], seed=3)
+    kvc = _kv(wl, 0)
+    n_phys = wl.k_pool.shape[0]
+    bounds = torch.full((n_phys, 2, 2, D), float("nan"), device=DEV).to(wl.k_pool.dtype)
+    s3r.page_bounds_update(kvc, bounds)
+    torch.cuda.synchronize()
+    ref = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), i32(wl.seq_lens[0]))
+    got = f64(bounds)
+    used = ~np.isnan(ref[:, 0, 0, 0])
+    assert np.array_equal(got[used], ref[used])
+    # Append one token per sequence and refresh only the touched pages.
+    kvc1 = _kv(wl, 1)
+    first = wl.seq_lens[0].clone()
+    s3r.page_bounds_update(kvc1, bounds, first_pos=first, max_pages_touched=1)
+    torch.cuda.synchronize()
+    ref1 = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), i32(wl.seq_lens[1]))
+    used1 = ~np.isnan(ref1[:, 0, 0, 0])
+    assert np.array_equal(f64(bounds)[used1], ref1[used1])
+
+
+SELECT_CASES = [
+    ("bf16", 128, 4, 2, 64, (700, 300, 40)),
+    ("bf16", 128, 2, 2, 160, (2000, 161)),
+    ("f32", 64, 2, 2, 64, (512, 513)),
+    ("bf16", 64, 8, 1, 32, (999, 1, 16)),
+]
+
+
+@pytest.mark.parametrize("kv,D,G,Hkv,budget,ctx", SELECT_CASES)
+def test_page_select_matches_oracle(kv, D, G, Hkv, budget, ctx):
+    wl = _make(_cfg(kv, D, G, Hkv, budget=budget, heavy=0), list(ctx), seed=11)
+    scale = 1.0 / np.sqrt(D)
+    for step in (0, 2):
+        kvc = _kv(wl, step)
+        bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=DEV)
+        s3r.page_bounds_update(kvc, bounds)
+        sel, nsel = s3r.page_select(kvc, bounds, wl.draft_q(step), budget, scale)
+        torch.cuda.synchronize()
+        rb = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), i32(wl.seq_lens[step]))
+        rsel, rn, rsc = oracle.page_select(rb, f64(wl.draft_q(step)), i32(wl.page_table),
+                                           i32(wl.seq_lens[step]), budget, scale)
+        check_pages(i32(sel), i32(nsel), rsel, rn, rsc, budget // 16)
+
+
+DRAFT_CASES = [
+    ("bf16", 128, 4, 2, 64, (700, 300, 40)),
+    ("bf16", 128, 2, 2, 1024, (3000, 100)),     # many selected pages: several splits
+    ("f32", 64, 2, 2, 64, (512, 300)),
+    ("bf16", 64, 8, 1, 48, (333, 15)),
+]
+
+
+@pytest.mark.parametrize("kv,D,G,Hkv,budget,ctx", DRAFT_CASES)
+def test_sparse_draft_matches_oracle(kv, D, G, Hkv, budget, ctx):
+    wl = _make(_cfg(kv, D, G, Hkv, budget=budget), list(ctx), seed=5)
+    scale = 1.0 / np.sqrt(D)
+    step = 1
+    kvc = _kv(wl, step)
+    bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(kvc, bounds)
+    sel, _ = s3r.page_select(kvc, bounds, wl.draft_q(step), budget, scale)
+    out = s3r.sparse_draft_attn(kvc, wl.draft_q(step), sel, scale)
+    torch.cuda.synchronize()
+    # the oracle attends over the GPU's own selection (selection parity is tested above)
+    ref = oracle.sparse_draft_attn(f64(wl.draft_q(step)), f64(wl.k_pool), f64(wl.v_pool),
+                                   i32(wl.page_table), i32(wl.seq_lens[step]), i32(sel), scale)
+    _check_attn(out, ref, kv)
+
+
+def test_sparse_draft_handcrafted_selection():
+    # -1 holes, unsorted ids and an id past the sequence are all skipped
+    wl = _make(_cfg("bf16", 128, 4, 2), [400, 200], seed=9)
+    kvc = _kv(wl, 0)
+    sel = torch.tensor([[[3, -1, 0, 24, 7], [20, 1, -1, -1, -1]],
+                        [[12, 11, 0, 2, 30], [-1, -1, -1, -1, -1]]], dtype=torch.int32, device=DEV)
+    out = s3r.sparse_draft_attn(kvc, wl.draft_q(0), sel, 0.1)
+    torch.cuda.synchronize()
+    n = np.array([oracle.n_pages(x, 16) for x in i32(wl.seq_lens[0])])
+    # every entry is read here (k = 5 <= n); ids >= n are skipped like -1
+    clean = np.where(i32(sel) < n[:, None, None], i32(sel), -1)
+    ref = oracle.sparse_draft_attn(f64(wl.draft_q(0)), f64(wl.k_pool), f64(wl.v_pool),
+                                   i32(wl.page_table), i32(wl.seq_lens[0]), clean, 0.1)
+    got = out.cpu().numpy()
+    assert np.all(got[1, 4:] == 0)            # an empty selection row gives zeros
+    ok = ~np.isnan(ref)
+    assert np.max(np.abs(got[ok] - ref[ok])) <= 1e-2
+
+
+def _sample_case(B, gamma, V, noise, seed, T=1.0):
+    g = torch.Generator().manual_seed(seed)
+    d = torch.randn((B, gamma, V), generator=g) * 2.0
+    t = torch.cat([d + torch.randn((B, gamma, V), generator=g) * noise,
+                   torch.randn((B, 1, V), generator=g) * 2.0], dim=1)
+    x = oracle.draw_draft_tokens(d.double().numpy(), T, seed=seed, offset=0)
+    return d, t, torch.from_numpy(x)
+
+
+@pytest.mark.parametrize("B,gamma,V,noise,T", [
+    (64, 4, 1024, 0.5, 1.0), (16, 6, 151936, 0.5, 1.0), (24, 8, 32000, 1.35, 1.0),
+    (32, 2, 5000, 3.0, 1.0), (8, 3, 4099, 0.7, 0.6), (40, 1, 100, 0.0, 1.0)])
+def test_spec_sample_matches_oracle(B, gamma, V, noise, T):
+    d, t, x = _sample_case(B, gamma, V, noise, seed=B + V, T=T)
+    out, n = s3r.spec_sample(d.to(DEV), t.to(DEV), x.to(DEV).int(), T, seed=0, offset=7)
+    torch.cuda.synchronize()
+    ro, rn, dec = oracle.spec_sample(d.double().numpy(), t.double().numpy(), x.numpy(), T, 0, 7)
+    full = check_tokens(i32(out), i32(n), ro, rn, dec)
+    assert full >= B - 1
+    if noise == 0.0:
+        assert np.all(i32(n) == gamma)
+
+
+def test_determinism_bitwise():
+    wl = _make(_cfg("bf16", 128, 4, 2, 6), [900, 300], seed=21)
+    kvc = _kv(wl, 6)
+    a = s3r.dense_verify_attn(kvc, wl.q_verify, 0.09)
+    b = s3r.dense_verify_attn(kvc, wl.q_verify, 0.09)
+    d, t, x = _sample_case(8, 4, 20000, 0.5, seed=3)
+    o1 = s3r.spec_sample(d.to(DEV), t.to(DEV), x.to(DEV).int(), 1.0, 1, 2)
+    o2 = s3r.spec_sample(d.to(DEV), t.to(DEV), x.to(DEV).int(), 1.0, 1, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(o1[0], o2[0]) and torch.equal(o1[1], o2[1])
+    # a different Philox offset gives a different stream
+    o3 = s3r.spec_sample(d.to(DEV), t.to(DEV), x.to(DEV).int(), 1.0, 1, 3)
+    assert not torch.equal(o1[0], o3[0]) or not torch.equal(o1[1], o3[1])
+
+
+def test_split_count_invariance():
+    wl = _make(_cfg("bf16", 128, 4, 2, 6), [1500, 700], seed=22)
+    outs = []
+    for hint in (0, 200, 60):
+        kvc = _kv(wl, 6, hint=hint)
+        outs.append(s3r.dense_verify_attn(kvc, wl.q_verify, 0.09).cpu())
+    for o in outs[1:]:
+        assert torch.max(torch.abs(o - outs[0])) <= 1e-5
+
+
+def test_unselected_pages_do_not_affect_draft():
+    wl = _make(_cfg("bf16", 128, 4, 2, 4, budget=64), [600, 450], seed=23)
+    kvc = _kv(wl, 0)
+    bounds = torch.empty((wl.k_pool.shape[0], 2, 2, 128), dtype=torch.bfloat16, device=DEV)
+    s3r.page_bounds_update(kvc, bounds)
+    sel, _ = s3r.page_select(kvc, bounds, wl.draft_q(0), 64, 0.09)
+    d0 = s3r.sparse_draft_attn(kvc, wl.draft_q(0), sel, 0.09).clone()
+    v0 = s3r.dense_verify_attn(kvc, wl.q_verify[:, :1].contiguous(), 0.09).clone()
+    # perturb every page no (sequence, kv head) selected
+    keep = set()
+    pt = wl.page_table.cpu()
+    for b in range(2):
+        for j in sel[b].flatten().tolist():
+            if j >= 0:
+                keep.add(int(pt[b, j]))
+    mask = torch.ones(wl.k_pool.shape[0], dtype=torch.bool)
+    mask[list(keep)] = False
+    idx = mask.nonzero().flatten().to(DEV)
+    wl.v_pool[idx] = (wl.v_pool[idx].float() + 1.0).to(torch.bfloat16)
+    d1 = s3r.sparse_draft_attn(kvc, wl.draft_q(0), sel, 0.09)
+    v1 = s3r.dense_verify_attn(kvc, wl.q_verify[:, :1].contiguous(), 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(d0, d1)
+    assert not torch.equal(v0, v1)
+
+
+def test_verify_row_equals_draft_over_all_pages():
+    gamma = 4
+    wl = _make(_cfg("bf16", 128, 4, 2, gamma, budget=4096), [555, 301], seed=24)
+    kvv = _kv(wl, gamma)
+    ver = s3r.dense_verify_attn(kvv, wl.q_verify, 0.09)
+    for i in range(gamma + 1):
+        kvd = _kv(wl, i)  # seq_len = S - gamma + i
+        sel = torch.arange(256, dtype=torch.int32, device=DEV).repeat(2, 2, 1).contiguous()
+        dr = s3r.sparse_draft_attn(kvd, wl.draft_q(i), sel, 0.09)
+        torch.cuda.synchronize()
+        assert torch.max(torch.abs(dr - ver[:, i])) <= 1e-5
+
+
+def test_edge_cases_empty_and_short():
+    gamma = 4
+    wl = _make(_cfg("bf16", 128, 4, 2, gamma), [40, 3, 1], seed=25)
+    seq = torch.tensor([0, 3, 16], dtype=torch.int32, device=DEV)  # empty, shorter than n_q, one page
+    kvc = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, seq, wl.cfg["Hq"])
+    out = s3r.dense_verify_attn(kvc, wl.q_verify, 0.1)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify_attn(f64(wl.q_verify), f64(wl.k_pool), f64(wl.v_pool),
+                                   i32(wl.page_table), seq.cpu().numpy(), 0.1)
+    assert np.all(out[0].cpu().numpy() == 0)
+    assert np.all(out[1, :2].cpu().numpy() == 0)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-2
+    bounds = torch.zeros((wl.k_pool.shape[0], 2, 2, 128), dtype=torch.bfloat16, device=DEV)
+    s3r.page_bounds_update(kvc, bounds)
+    sel, n = s3r.page_select(kvc, bounds, wl.draft_q(0), 32, 0.1)
+    torch.cuda.synchronize()
+    assert i32(n).tolist() == [0, 1, 1]
+    assert i32(sel)[0].tolist() == [[-1, -1], [-1, -1]]
+    assert i32(sel)[1].tolist() == [[0, -1], [0, -1]]
+    dr = s3r.sparse_draft_attn(kvc, wl.draft_q(0), sel, 0.1)
+    torch.cuda.synchronize()
+    assert np.all(dr[0].cpu().numpy() == 0)
