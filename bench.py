@@ -1,0 +1,320 @@
+"""Benchmark one S3R round (the whole hot path) on one MI355X.
+
+A step is one round of "S3R: Fast and Faithful RL Rollouts via
+Self-Sparse Speculative Decoding" (Abstract) for one attention layer:
+  for j in 0..gamma-1: page_bounds_update (tail page) -> page_select ->
+                       sparse_draft_attn (query position L-1+j)
+  dense_verify_attn (gamma+1 causal queries over the complete KV)
+  spec_sample (accept/reject, residual or bonus draw)
+over the Qwen3-8B-shaped layer: bf16 paged KV, 32 q / 8 kv heads, head dim 128,
+batch 32, context 32768, page 16, budget 2048 tokens, gamma 6, vocab 151936,
+4 planted high-norm pages per sequence. Inputs are seeded synthetic tensors,
+resident in HBM before timing. The step is captured once into a HIP graph
+and replayed.
+
+Prints one JSON line. `value` is the step's algorithmic HBM bytes (KV, page
+bounds and logits each counted once) over the measured step time, in GB/s;
+`accepted_tokens_per_s` is committed tokens (accepted + 1 per sequence) per
+second. `roofline` covers the dominant launch (dense verify), timed with HIP
+events on the stream it runs on; `cpu_baseline` is the fp64 oracle on a
+bounded slice of the same workload, on the host.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "draft+verify attention KV GB/s (% of HBM peak); accepted tokens/s at 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="qwen3_8b")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="rough budget of oracle CPU work for the baseline")
+    return p.parse_args()
+
+
+def step_bytes(cfg, ctx):
+    """Algorithmic HBM bytes of one round, summed over sequences."""
+    P, D, Hkv, Hq, gamma, V = (cfg[k] for k in ("P", "D", "Hkv", "Hq", "gamma", "V"))
+    esz = 2 if cfg["kv_dtype"] == "bf16" else 4
+    kv_tok = 2 * Hkv * D * esz                  # K + V of one token, all kv heads
+    bound_page = 2 * Hkv * D * esz              # min + max of one page, all kv heads
+    k = cfg["budget"] // P
+    parts = dict(select=0, draft=0, bounds=0, verify=0, sample=0, q_out=0)
+    for L in ctx:
+        for j in range(gamma):
+            n = -(-(L + j) // P)
+            parts["select"] += n * bound_page
+            parts["draft"] += min(k, n) * P * kv_tok
+            parts["bounds"] += P * Hkv * D * esz + bound_page   # tail page read + write
+            parts["q_out"] += 2 * Hq * D * esz
+        parts["verify"] += (L + gamma) * kv_tok
+        parts["q_out"] += 2 * (gamma + 1) * Hq * D * esz
+        parts["sample"] += (2 * gamma + 1) * V * 4
+    return parts
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.exit(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+                 "(the S3R hot path shards by sequence with no exchange; see DESIGN.md)")
+
+    import numpy as np
+    import torch
+
+    import self_sparse_speculative_paged_amd as s3r
+    from s3r_inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = make_workload(args.config, device=dev, seed=0)
+    cfg = wl.cfg
+    B, Hq, Hkv, D, P, gamma, V = (cfg[k] for k in ("B", "Hq", "Hkv", "D", "P", "gamma", "V"))
+    budget, T = cfg["budget"], cfg["temperature"]
+    k = budget // P
+    scale = 1.0 / math.sqrt(D)
+    ctx = [int(x) for x in wl.ctx]
+    total_pages = sum(-(-(L + gamma) // P) for L in ctx)
+
+    kv = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[0], Hq,
+                          total_pages_hint=total_pages)
+    n_phys = wl.k_pool.shape[0]
+    bounds = torch.empty((n_phys, Hkv, 2, D), dtype=wl.k_pool.dtype, device=dev)
+    s3r.page_bounds_update(kv, bounds)  # set-up: every page
+    first_pos = [(s - 1).contiguous() for s in wl.seq_lens]
+    q_draft = [wl.draft_q(j) for j in range(gamma)]
+    sel = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev)
+    d_out = torch.empty((gamma, B, Hq, D), dtype=torch.bfloat16, device=dev)
+    v_out = torch.empty((B, gamma + 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws_sel = torch.empty(max(1, s3r.page_select_workspace(kv, budget)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, s3r.attn_workspace(kv, 1, k)), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(max(1, s3r.attn_workspace(kv, gamma + 1, wl.max_pages)), dtype=torch.uint8,
+                       device=dev)
+    ws_s = torch.empty(max(1, s3r.spec_sample_workspace(B, gamma, V)), dtype=torch.uint8, device=dev)
+    out_tok = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def draft_step(j):
+        kv.set_seq_lens(wl.seq_lens[j])
+        s3r.page_bounds_update(kv, bounds, first_pos=first_pos[j], max_pages_touched=1)
+        s3r.page_select(kv, bounds, q_draft[j], budget, scale, sel, nsel, workspace=ws_sel)
+        s3r.sparse_draft_attn(kv, q_draft[j], sel, scale, out=d_out[j], workspace=ws_d)
+
+    def verify():
+        kv.set_seq_lens(wl.seq_lens[gamma])
+        s3r.dense_verify_attn(kv, wl.q_verify, scale, out=v_out, workspace=ws_v)
+
+    def sample(offset):
+        s3r.spec_sample(wl.draft_logits, wl.target_logits, wl.draft_tokens, T, 0, offset,
+                        out_tokens=out_tok, num_accepted=n_acc, workspace=ws_s)
+
+    def one_round(offset=0):
+        for j in range(gamma):
+            draft_step(j)
+        verify()
+        sample(offset)
+
+    # eager warm-up, and the accepted-length statistics over several Philox offsets
+    for w in range(max(1, args.warmup)):
+        one_round(w)
+    acc = []
+    for off in range(8):
+        sample(off)
+        acc.append(n_acc.clone())
+    torch.cuda.synchronize()
+    acc = torch.stack(acc).float()
+    mean_committed = float((acc + 1).sum(dim=1).mean())  # tokens committed per round, all sequences
+
+    runner = one_round
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            one_round(0)
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            one_round(0)
+        runner = g.replay
+        for _ in range(max(1, args.warmup)):
+            runner()
+    torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        runner()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # Per-launch timing of each entry point (eager, events on the launch stream).
+    def time_call(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3  # us
+
+    reps = max(5, args.steps)
+    kv.set_seq_lens(wl.seq_lens[0])
+    t_select = time_call(lambda: s3r.page_select(kv, bounds, q_draft[0], budget, scale, sel, nsel,
+                                                 workspace=ws_sel), reps)
+    t_draft = time_call(lambda: s3r.sparse_draft_attn(kv, q_draft[0], sel, scale, out=d_out[0],
+                                                      workspace=ws_d), reps)
+    t_bounds = time_call(lambda: s3r.page_bounds_update(kv, bounds, first_pos=first_pos[0],
+                                                        max_pages_touched=1), reps)
+    kv.set_seq_lens(wl.seq_lens[gamma])
+    t_verify = time_call(lambda: s3r.dense_verify_attn(kv, wl.q_verify, scale, out=v_out,
+                                                       workspace=ws_v), reps)
+    t_sample = time_call(lambda: sample(0), reps)
+
+    parts = step_bytes(cfg, ctx)
+    total_bytes = sum(parts.values())
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    verify_gbs = parts["verify"] / (t_verify * 1e-6) / 1e9
+    per_step_draft = parts["draft"] / gamma
+    draft_gbs = per_step_draft / (t_draft * 1e-6) / 1e9
+    dv_us = gamma * t_draft + t_verify
+    dv_gbs = (parts["draft"] + parts["verify"]) / (dv_us * 1e-6) / 1e9
+
+    traffic = read_counter_traffic(args.config)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 KV/Q, N(0,2)+noise fp32 logits)",
+        "config": {"workload": f"{args.config}_layer", "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "context": ctx[0] if len(set(ctx)) == 1 else "ragged",
+                   "page": P, "budget_tokens": budget, "gamma": gamma, "vocab": V,
+                   "graph": not args.no_graph},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "accepted_tokens_per_s": round(mean_committed / (ms * 1e-3), 1),
+        "mean_accepted_per_seq": round(float(acc.mean()), 3),
+        "draft_verify_kv_gbs": round(dv_gbs, 1),
+        "draft_kv_gbs": round(draft_gbs, 1),
+        "verify_kv_gbs": round(verify_gbs, 1),
+        "step_bytes": {k2: int(v2) for k2, v2 in parts.items()},
+        "launch_us": {"page_bounds_update": round(t_bounds, 2), "page_select": round(t_select, 2),
+                      "sparse_draft_attn": round(t_draft, 2),
+                      "dense_verify_attn": round(t_verify, 2), "spec_sample": round(t_sample, 2)},
+        "roofline": {"kernel": "dense_verify_attn (attn_bf16_kernel + split combine)",
+                     "bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def read_counter_traffic(config):
+    """HBM bytes per verify launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"counters_dense_verify_{config}.txt")
+    src = os.path.join(ROOT, "self_sparse_speculative_paged_amd", "csrc", "s3r_attn.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16") != digest:
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, cfg, budget_s):
+    """The oracle, as it stands, on (sequence, kv head) slices of the round until
+    about `budget_s` seconds of single-threaded CPU work: per slice gamma x
+    (page_select + sparse draft), the slice's dense verify and the sequence's
+    spec_sample. Reported as algorithmic GB/s over the slices done."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    P, D, Hkv, Hq, gamma, V = (cfg[k] for k in ("P", "D", "Hkv", "Hq", "gamma", "V"))
+    G = Hq // Hkv
+    esz = 2 if cfg["kv_dtype"] == "bf16" else 4
+    scale = 1.0 / math.sqrt(D)
+    k = cfg["budget"] // P
+    bytes_done, elapsed, slices = 0, 0.0, 0
+    for b in range(cfg["B"]):
+        L = int(wl.ctx[b])
+        n = -(-(L + gamma) // P)
+        idx = wl.page_table[b, :n].long()
+        pt = np.arange(n, dtype=np.int64)[None, :]
+        dl = wl.draft_logits[b:b + 1].to("cpu", torch.float64).numpy()
+        tl = wl.target_logits[b:b + 1].to("cpu", torch.float64).numpy()
+        xt = wl.draft_tokens[b:b + 1].cpu().numpy()
+        for h in range(Hkv):
+            K = wl.k_pool.index_select(0, idx)[:, h:h + 1].to("cpu", torch.float64).numpy()
+            Vv = wl.v_pool.index_select(0, idx)[:, h:h + 1].to("cpu", torch.float64).numpy()
+            q_ver = wl.q_verify[b:b + 1, :, h * G:(h + 1) * G].to("cpu", torch.float64).numpy()
+            bounds = oracle.page_bounds(K, pt, np.array([L + gamma]))  # set-up, untimed
+            t0 = time.perf_counter()
+            with threadpool_limits(limits=1):
+                for j in range(gamma):
+                    lens = np.array([L + j])
+                    qd = q_ver[:, j]
+                    sel, _, _ = oracle.page_select(bounds, qd, pt, lens, cfg["budget"], scale, P)
+                    oracle.sparse_draft_attn(qd, K, Vv, pt, lens, sel, scale)
+                    nj = -(-(L + j) // P)
+                    bytes_done += nj * 2 * D * esz + min(k, nj) * P * 2 * D * esz
+                oracle.dense_verify_attn(q_ver, K, Vv, pt, np.array([L + gamma]), scale)
+                bytes_done += (L + gamma) * 2 * D * esz
+                if h == 0:
+                    oracle.spec_sample(dl, tl, xt, cfg["temperature"], 0, 0)
+                    bytes_done += (2 * gamma + 1) * V * 4
+            elapsed += time.perf_counter() - t0
+            slices += 1
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    return {"value": round(bytes_done / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(elapsed, 2),
+            "sample": f"{slices} (sequence, kv head) slices of {cfg['B']}x{Hkv}, each: {gamma} draft "
+                      f"steps (page_select + sparse attention), dense verify of {gamma + 1} queries x "
+                      f"{G} heads over the full context, plus spec_sample (vocab {V}) once per "
+                      f"sequence; fp64 NumPy, 1 thread"}
+
+
+if __name__ == "__main__":
+    main()
