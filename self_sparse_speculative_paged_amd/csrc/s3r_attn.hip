@@ -112,12 +112,15 @@ __device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint1
 #pragma unroll
     for (int s = 0; s < kD / 32; ++s) t.k[mb][s] = *reinterpret_cast<const bf16x8*>(base + 8 * s);
   }
-  // O^T A operand: lane holds V^T[d = 16*mb + l16][window tokens 8*g4 .. 8*g4+7].
+  // K loads cover 64 of each row's 256 bytes per instruction, so they stay
+  // cached: the four k-step loads of a row share its two 128-byte lines.
+  // O^T A operand: lane holds V^T[d = 16*mb + l16][window tokens 8*g4 .. 8*g4+7];
+  // each load instruction covers two whole 512-byte runs, streamed (nontemporal).
   const int vphys = (g4 >= 2) ? w.physB : w.physA;
   const uint16_t* vbase = vp + ((size_t)vphys * Hkv + h) * kD * kPage + l16 * kPage + 8 * (g4 & 1);
 #pragma unroll
   for (int mb = 0; mb < kD / 16; ++mb)
-    t.v[mb] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)16 * mb * kPage);
+    t.v[mb] = load_nt16<bf16x8>(vbase + (size_t)16 * mb * kPage);
 }
 
 template <int kD, int kNB>
@@ -174,8 +177,16 @@ __device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
   }
 }
 
+// One row block (the draft, small verify groups) fits two waves per SIMD with a
+// 2-stage pipeline; more row blocks run one wave per SIMD with deeper stages.
+template <int kNB>
+constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : 2); }
+template <int kNB>
+constexpr int bf16_waves_per_simd() { return kNB == 1 ? 2 : 1; }
+
 template <int kD, int kNB, bool kSparse>
-__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bf16_waves_per_simd<kNB>(), 8)))
+void attn_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x % a.n_splits;
   const int bh = blockIdx.x / a.n_splits;
@@ -223,38 +234,66 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
   }
 
   const int min_qpos = seq_len - a.nq;
-  const int fallback = pt[0];
-  auto pages_of = [&](int jj) {
+  // Resolve every window's pages once: lanes look up the item's page ids in
+  // parallel (selection entry, then page table) into an LDS table, so the
+  // pipeline below never waits on a dependent page-table load.
+  extern __shared__ int4 win_tab[];  // per window {lpA, lpB, physA, physB}
+  const int n_win = (j1 - j0 + 1) / 2;
+  {
+    const int fallback = pt[0];
+    for (int w0 = 0; w0 < n_win; w0 += 64) {
+      const int wi = w0 + lane;
+      if (wi < n_win) {
+        const int jj = j0 + 2 * wi;
+        int4 e;
+        e.x = logical_page<kSparse>(sel, jj, n_pages);
+        e.y = (jj + 1 < j1) ? logical_page<kSparse>(sel, jj + 1, n_pages) : -1;
+        e.z = e.x >= 0 ? pt[e.x] : fallback;
+        e.w = e.y >= 0 ? pt[e.y] : e.z;
+        win_tab[wi] = e;
+      }
+    }
+  }
+  auto pages_of = [&](int wi) {
+    const int4 e = win_tab[wi];
     WindowPages w;
-    w.lpA = logical_page<kSparse>(sel, jj, n_pages);
-    w.lpB = (jj + 1 < j1) ? logical_page<kSparse>(sel, jj + 1, n_pages) : -1;
-    w.physA = w.lpA >= 0 ? pt[w.lpA] : fallback;
-    w.physB = w.lpB >= 0 ? pt[w.lpB] : w.physA;
+    w.lpA = __builtin_amdgcn_readfirstlane(e.x);
+    w.lpB = __builtin_amdgcn_readfirstlane(e.y);
+    w.physA = __builtin_amdgcn_readfirstlane(e.z);
+    w.physB = __builtin_amdgcn_readfirstlane(e.w);
     return w;
   };
   auto masked = [&](const WindowPages& w) {
     return w.lpA < 0 || w.lpB < 0 || 16 * max(w.lpA, w.lpB) + 15 > min_qpos;
   };
 
-  // Two tiles in flight: the loads of window n+1 are issued before window n is
-  // computed.
-  Bf16Tile<kD, kNB> t0, t1;
-  WindowPages w0 = pages_of(j0), w1;
-  load_bf16_tile<kD, kNB>(t0, kp, vp, a.Hkv, h, w0);
-  for (int jj = j0; jj < j1; jj += 4) {
-    const bool has1 = jj + 2 < j1;
-    if (has1) {
-      w1 = pages_of(jj + 2);
-      load_bf16_tile<kD, kNB>(t1, kp, vp, a.Hkv, h, w1);
+  // kStages-deep register pipeline: while window i is computed, the loads of
+  // windows i+1 .. i+kStages-1 are in flight. Three stages fit the 512
+  // registers of a single wave per SIMD up to two row blocks.
+  constexpr int kStages = bf16_stages<kNB>();
+  Bf16Tile<kD, kNB> t[kStages];
+  WindowPages w[kStages];
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < n_win) {
+      w[s] = pages_of(s);
+      load_bf16_tile<kD, kNB>(t[s], kp, vp, a.Hkv, h, w[s]);
     }
-    compute_bf16_tile<kD, kNB>(t0, qb, qpos, w0, masked(w0), a.scale_log2, m_run, l_run, acc);
-    if (!has1) break;
-    const bool has0 = jj + 4 < j1;
-    if (has0) {
-      w0 = pages_of(jj + 4);
-      load_bf16_tile<kD, kNB>(t0, kp, vp, a.Hkv, h, w0);
+  }
+  for (int base = 0; base < n_win; base += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      const int i = base + s;
+      if (i >= n_win) break;
+      const int ip = i + kStages - 1;
+      if (ip < n_win) {
+        w[(s + kStages - 1) % kStages] = pages_of(ip);
+        load_bf16_tile<kD, kNB>(t[(s + kStages - 1) % kStages], kp, vp, a.Hkv, h,
+                                w[(s + kStages - 1) % kStages]);
+      }
+      compute_bf16_tile<kD, kNB>(t[s], qb, qpos, w[s], masked(w[s]), a.scale_log2, m_run, l_run,
+                                 acc);
     }
-    compute_bf16_tile<kD, kNB>(t1, qb, qpos, w1, masked(w1), a.scale_log2, m_run, l_run, acc);
   }
   write_partial<kD, kNB>(a, b, h, split, m_run, l_run, acc);
 }
@@ -275,14 +314,14 @@ __device__ __forceinline__ void load_f32_tile(F32Tile<kD>& t, const float* kp, c
   const float* kb = kp + (((size_t)phys * Hkv + h) * kPage + l16) * kD + (kD / 4) * g4;
 #pragma unroll
   for (int s = 0; s < kD / 16; ++s) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(kb + 4 * s);
+    const f32x4 v = load_nt16<f32x4>(kb + 4 * s);
 #pragma unroll
     for (int e = 0; e < 4; ++e) t.k[4 * s + e] = v[e];
   }
   const float* vb = vp + ((size_t)phys * Hkv + h) * kD * kPage + l16 * kPage + 4 * g4;
 #pragma unroll
   for (int mb = 0; mb < kD / 16; ++mb)
-    t.v[mb] = *reinterpret_cast<const f32x4*>(vb + (size_t)16 * mb * kPage);
+    t.v[mb] = load_nt16<f32x4>(vb + (size_t)16 * mb * kPage);
 }
 
 template <int kD, int kNB, bool kSparse>
@@ -385,18 +424,37 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const int ns = (n_items + a.pages_per_split - 1) / a.pages_per_split;
   const size_t item0 = ((size_t)b * a.Hkv + h) * a.n_splits;
 
+  // Splits are folded 8 at a time with all their loads in flight together.
+  constexpr int kBatch = 8;
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((item0 + s) * a.rows + row) * 2]);
   float o[kD / 64] = {};
   float den = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < ns; ++s) {
-      const size_t r = (item0 + s) * a.rows + row;
-      const float w = __builtin_amdgcn_exp2f(a.part_ml[r * 2] - M);
-      den += w * a.part_ml[r * 2 + 1];
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    float m[kBatch], l[kBatch], ov[kBatch][kD / 64];
 #pragma unroll
-      for (int e = 0; e < kD / 64; ++e) o[e] += w * a.part_o[r * kD + lane + 64 * e];
+    for (int u = 0; u < kBatch; ++u) {
+      const size_t r = (item0 + min(s0 + u, ns - 1)) * a.rows + row;
+      m[u] = s0 + u < ns ? a.part_ml[r * 2] : kNegInf;
+      l[u] = a.part_ml[r * 2 + 1];
+#pragma unroll
+      for (int e = 0; e < kD / 64; ++e) ov[u][e] = a.part_o[r * kD + lane + 64 * e];
     }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, m[u]);
+    if (Mb == kNegInf) continue;
+    const float c = __builtin_amdgcn_exp2f(M - Mb);  // rescale what was folded so far
+    den *= c;
+#pragma unroll
+    for (int e = 0; e < kD / 64; ++e) o[e] *= c;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = __builtin_amdgcn_exp2f(m[u] - Mb);
+      den += w * l[u];
+#pragma unroll
+      for (int e = 0; e < kD / 64; ++e) o[e] += w * ov[u][e];
+    }
+    M = Mb;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const size_t obase = (((size_t)b * a.nq + i) * a.Hq + g) * kD;
@@ -413,8 +471,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 template <int kD, int kNB, bool kSparse>
 hipError_t launch_typed(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_splits));
-  if (dt == S3R_BF16)
-    hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse>), grid, dim3(64), 0, stream, a);
+  if (dt == S3R_BF16) {
+    const size_t lds = sizeof(int4) * (size_t)((a.pages_per_split + 1) / 2);
+    hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse>), grid, dim3(64), lds, stream, a);
+  }
   else
     hipLaunchKernelGGL((attn_f32_kernel<kD, kNB, kSparse>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -438,14 +498,16 @@ hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
 }  // namespace
 
 SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items) {
-  // Aim for ~8 resident waves on each of the 256 CUs.
-  constexpr long kTargetItems = 2048;
+  // As many items as resident waves: 256 CUs x 4 SIMDs x (2 waves per SIMD for
+  // one MFMA row block, 1 otherwise).
   constexpr long kMinPagesPerSplit = 16;
+  constexpr long kMaxPagesPerSplit = 4096;  // LDS window table <= 32 KB
   SplitPlan p{};
   const long B = kv.num_seqs, Hkv = kv.num_kv_heads;
   const int G = kv.num_q_heads / kv.num_kv_heads;
   p.rows = G * n_queries;
   p.row_blocks = (p.rows + 15) / 16;
+  const long kTargetItems = p.row_blocks == 1 ? 2048 : 1024;
   long total = (long)B * max_items;
   if (kv.total_pages_hint > 0 && kv.total_pages_hint < total) total = kv.total_pages_hint;
   const double avg = (double)total / (double)B;
@@ -456,6 +518,7 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
   pps = (pps + 1) & ~1L;
   const long cap = ((long)max_items + 1) & ~1L;
   if (pps > cap) pps = cap;
+  if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   p.pages_per_split = (int32_t)pps;
   p.n_splits = (int32_t)((max_items + pps - 1) / pps);
   const size_t items = (size_t)B * Hkv * p.n_splits;

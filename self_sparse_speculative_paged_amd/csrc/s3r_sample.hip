@@ -60,7 +60,10 @@ struct Layout {
   double* sum;     // [B][R][C] chunk sum of exp((x - chunk max) / T)
   double* wsum;    // [B][C] chunk sum of the residual/bonus weights
   double* psum;    // [B][C] chunk sum of the target row's probabilities
+  double* iz;      // [B][R] 1 / row normaliser, as the residual pass used it
   float* cmax;     // [B][R][C] chunk max logit
+  float* rmax;     // [B][R] row max logit
+  int* nacc;       // [B] accepted drafts
 };
 
 __host__ __device__ inline Layout layout_of(void* ws, int B, int gamma, int C) {
@@ -73,7 +76,13 @@ __host__ __device__ inline Layout layout_of(void* ws, int B, int gamma, int C) {
   p += sizeof(double) * B * C;
   l.psum = reinterpret_cast<double*>(p);
   p += sizeof(double) * B * C;
+  l.iz = reinterpret_cast<double*>(p);
+  p += sizeof(double) * B * R;
   l.cmax = reinterpret_cast<float*>(p);
+  p += sizeof(float) * B * R * C;
+  l.rmax = reinterpret_cast<float*>(p);
+  p += sizeof(float) * B * R;
+  l.nacc = reinterpret_cast<int*>(p);
   return l;
 }
 
@@ -83,9 +92,11 @@ __device__ __forceinline__ const float* row_ptr(const SampleArgs& a, int b, int 
                      : a.target_logits + ((size_t)b * (a.gamma + 1) + (r - a.gamma)) * a.V;
 }
 
-// exp((x - m) / T) with the argument formed in fp64 and rounded once to fp32.
-__device__ __forceinline__ float scaled_exp(float x, double m, double inv_t) {
-  return expf((float)(((double)x - m) * inv_t));
+// exp((x - m) / T) as 2^((x - m) * log2(e) / T): one v_exp_f32 per element.
+// The argument's fp32 rounding moves each term by ~1e-7 relative at the
+// magnitudes that carry mass; the sums are accumulated in fp64.
+__device__ __forceinline__ float scaled_exp(float x, float m, float c_log2) {
+  return __builtin_amdgcn_exp2f((x - m) * c_log2);
 }
 
 template <typename T>
@@ -119,64 +130,109 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(SampleArgs a) {
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   float x[kPerThread];
   float m = -__builtin_huge_valf();
+  // Thread t owns tokens lo + 4*(t + 256*k) .. +3 (16-byte loads when the row
+  // is 16-byte aligned, scalar loads otherwise).
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int t = lo + threadIdx.x + kThreads * k;
-    x[k] = t < hi ? row[t] : -__builtin_huge_valf();
-    m = fmaxf(m, x[k]);
+  for (int k = 0; k < kPerThread / 4; ++k) {
+    const int t = lo + 4 * (threadIdx.x + kThreads * k);
+    if (vec && t + 3 < hi) {
+      const f32x4 v = load_nt16<f32x4>(row + t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * k + e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * k + e] = t + e < hi ? row[t + e] : -__builtin_huge_valf();
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, x[4 * k + e]);
   }
   m = block_reduce_max(m, redf);
-  const double inv_t = 1.0 / (double)a.temperature;
-  double s = 0.0;
+  const float c_log2 = 1.4426950408889634f / a.temperature;
+  float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k)
-    if (lo + threadIdx.x + kThreads * k < hi) s += (double)scaled_exp(x[k], (double)m, inv_t);
-  s = block_reduce_sum<double>(s, redd);
+  for (int k = 0; k < kPerThread; ++k) s += scaled_exp(x[k], m, c_log2);  // -inf pads give 0
+  const double sd = block_reduce_sum<double>((double)s, redd);
   if (threadIdx.x == 0) {
     const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
     const size_t idx = ((size_t)b * (2 * a.gamma + 1) + r) * a.n_chunks + c;
-    L.sum[idx] = s;
+    L.sum[idx] = sd;
     L.cmax[idx] = m;
   }
 }
 
 // Per-block view of one sequence's round: row normalisers and the accept scan.
 struct Round {
-  double M[2 * 16 + 1];
-  double Z[2 * 16 + 1];
-  int n;  // accepted drafts
+  float M[2 * 16 + 1];    // row max logit
+  double Z[2 * 16 + 1];   // sum over the row of 2^((x - M) * log2(e) / T)
+  double iZ[2 * 16 + 1];
+  int accept[16];
+  int n;                  // accepted drafts
 };
 
-// Every thread r < 2*gamma+1 folds row r's chunk statistics in chunk order;
-// thread 0 then runs the accept scan. Identical in every block that calls it.
+// Threads r < 2*gamma+1 fold row r's chunk statistics in chunk order; threads
+// i < gamma then decide draft i (gathered logits, fp64 ratio, Philox uniform)
+// and thread 0 takes the first rejection. Identical in every calling block.
 __device__ void round_decision(const SampleArgs& a, int b, Round& rd) {
   const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
   const int R = 2 * a.gamma + 1;
-  const double inv_t = 1.0 / (double)a.temperature;
-  const int r = threadIdx.x;
-  if (r < R) {
-    const size_t base = ((size_t)b * R + r) * a.n_chunks;
-    double M = -__builtin_huge_val();
-    for (int c = 0; c < a.n_chunks; ++c) M = fmax(M, (double)L.cmax[base + c]);
-    double Z = 0.0;
-    for (int c = 0; c < a.n_chunks; ++c) Z += L.sum[base + c] * exp(((double)L.cmax[base + c] - M) * inv_t);
-    rd.M[r] = M;
-    rd.Z[r] = Z;
+  const double c_log2 = 1.4426950408889634 / (double)a.temperature;
+  // Wave w folds rows w, w+4, ...: lane l takes chunks l, l+64, ... and the
+  // lanes are combined by a fixed butterfly (deterministic). The loads of all
+  // the wave's rows are issued before any is folded.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kRowsPerWave = (2 * 16 + 1 + kThreads / 64 - 1) / (kThreads / 64);
+  for (int c0 = 0; c0 == 0 || c0 < a.n_chunks; c0 += 64) {
+    float cm[kRowsPerWave];
+    double cs[kRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = wave + (kThreads / 64) * k;
+      const int c = c0 + lane;
+      const bool ok = r < R && c < a.n_chunks;
+      const size_t idx = ((size_t)b * R + (ok ? r : 0)) * a.n_chunks + (ok ? c : 0);
+      cm[k] = ok ? L.cmax[idx] : -__builtin_huge_valf();
+      cs[k] = ok ? L.sum[idx] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = wave + (kThreads / 64) * k;
+      if (r >= R) break;
+      float M = cm[k];
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
+      double Z = cs[k] > 0.0 ? cs[k] * exp2(((double)cm[k] - (double)M) * c_log2) : 0.0;
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) Z += __shfl_xor(Z, x, 64);
+      if (lane == 0) {
+        if (c0 == 0) {
+          rd.M[r] = M;
+          rd.Z[r] = Z;
+        } else {  // more than 64 chunks: fold this pass into the running values
+          const float Mn = fmaxf(rd.M[r], M);
+          rd.Z[r] = rd.Z[r] * exp2(((double)rd.M[r] - Mn) * c_log2) +
+                    Z * exp2(((double)M - Mn) * c_log2);
+          rd.M[r] = Mn;
+        }
+        rd.iZ[r] = 1.0 / rd.Z[r];
+      }
+    }
+  }
+  __syncthreads();
+  const int i = threadIdx.x;
+  if (i < a.gamma) {
+    const int x = a.draft_tokens[(size_t)b * a.gamma + i];
+    const double lt = row_ptr(a, b, a.gamma + i)[x];
+    const double ld = row_ptr(a, b, i)[x];
+    const double p = exp2((lt - (double)rd.M[a.gamma + i]) * c_log2) / rd.Z[a.gamma + i];
+    const double q = exp2((ld - (double)rd.M[i]) * c_log2) / rd.Z[i];
+    const double u = philox_uniform(a.seed, a.offset, b, i, 0);
+    rd.accept[i] = q > 0.0 ? (u < p / q) : (p > 0.0);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int n = 0;
-    for (int i = 0; i < a.gamma; ++i) {
-      const int x = a.draft_tokens[(size_t)b * a.gamma + i];
-      const double lt = row_ptr(a, b, a.gamma + i)[x];
-      const double ld = row_ptr(a, b, i)[x];
-      const double p = exp((lt - rd.M[a.gamma + i]) * inv_t) / rd.Z[a.gamma + i];
-      const double q = exp((ld - rd.M[i]) * inv_t) / rd.Z[i];
-      const double u = philox_uniform(a.seed, a.offset, b, i, 0);
-      const bool accept = q > 0.0 ? (u < p / q) : (p > 0.0);
-      if (!accept) break;
-      ++n;
-    }
+    while (n < a.gamma && rd.accept[n]) ++n;
     rd.n = n;
   }
   __syncthreads();
@@ -186,13 +242,13 @@ __device__ void round_decision(const SampleArgs& a, int b, Round& rd) {
 // p_gamma for the bonus. `p_out` receives p (the fallback when the residual
 // has no mass).
 __device__ __forceinline__ double draw_weight(const SampleArgs& a, const Round& rd, int b, int t,
-                                              double inv_t, double* p_out) {
+                                              float c_log2, double* p_out) {
   const int n = rd.n;
   const int tr = a.gamma + n;
-  const double p = (double)scaled_exp(row_ptr(a, b, tr)[t], rd.M[tr], inv_t) / rd.Z[tr];
+  const double p = (double)scaled_exp(row_ptr(a, b, tr)[t], rd.M[tr], c_log2) * rd.iZ[tr];
   *p_out = p;
   if (n == a.gamma) return p;
-  const double q = (double)scaled_exp(row_ptr(a, b, n)[t], rd.M[n], inv_t) / rd.Z[n];
+  const double q = (double)scaled_exp(row_ptr(a, b, n)[t], rd.M[n], c_log2) * rd.iZ[n];
   return p > q ? p - q : 0.0;
 }
 
@@ -201,70 +257,133 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
   __shared__ double redd[4];
   const int c = blockIdx.x, b = blockIdx.y;
   round_decision(a, b, rd);
-  const double inv_t = 1.0 / (double)a.temperature;
+  const float c_log2 = 1.4426950408889634f / a.temperature;
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
+  // All of this thread's logits are loaded before any is used.
+  const int tr = a.gamma + rd.n, dr = rd.n < a.gamma ? rd.n : tr;
+  const float* trow = row_ptr(a, b, tr);
+  const float* drow = row_ptr(a, b, dr);
+  float xt[kPerThread], xd[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int t = lo + threadIdx.x + kThreads * k;
+    xt[k] = t < hi ? trow[t] : -__builtin_huge_valf();
+    xd[k] = t < hi ? drow[t] : -__builtin_huge_valf();
+  }
+  const bool bonus = rd.n == a.gamma;
   double w = 0.0, ps = 0.0;
-  for (int t = lo + threadIdx.x; t < hi; t += kThreads) {
-    double p;
-    w += draw_weight(a, rd, b, t, inv_t, &p);
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const double p = (double)scaled_exp(xt[k], rd.M[tr], c_log2) * rd.iZ[tr];
+    const double q = bonus ? 0.0 : (double)scaled_exp(xd[k], rd.M[dr], c_log2) * rd.iZ[dr];
+    w += p > q ? p - q : 0.0;
     ps += p;
   }
   w = block_reduce_sum<double>(w, redd);
   ps = block_reduce_sum<double>(ps, redd);
+  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
   if (threadIdx.x == 0) {
-    const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
     L.wsum[(size_t)b * a.n_chunks + c] = w;
     L.psum[(size_t)b * a.n_chunks + c] = ps;
   }
+  if (c == 0) {  // the finalize pass reuses this block's decision
+    const int R = 2 * a.gamma + 1;
+    if (threadIdx.x < (unsigned)R) {
+      L.rmax[(size_t)b * R + threadIdx.x] = rd.M[threadIdx.x];
+      L.iz[(size_t)b * R + threadIdx.x] = rd.iZ[threadIdx.x];
+    }
+    if (threadIdx.x == 0) L.nacc[b] = rd.n;
+  }
+}
+
+// Inclusive prefix sum of one double per thread over the block, in thread
+// order (Hillis-Steele in LDS; the addition order is fixed).
+__device__ double block_inclusive_scan(double v, double* buf) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (int d = 1; d < kThreads; d <<= 1) {
+    const double y = threadIdx.x >= (unsigned)d ? buf[threadIdx.x - d] : 0.0;
+    __syncthreads();
+    buf[threadIdx.x] += y;
+    __syncthreads();
+  }
+  return buf[threadIdx.x];
 }
 
 __global__ __launch_bounds__(kThreads) void finalize_kernel(SampleArgs a) {
   __shared__ Round rd;
   __shared__ double scan[kThreads];
-  __shared__ int s_chunk, s_use_p, s_fallback, s_first, s_last;
-  __shared__ double s_base, s_target;
+  __shared__ int s_chunk, s_first, s_last, s_pos_last;
   const int b = blockIdx.x;
-  round_decision(a, b, rd);
   const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-  const double inv_t = 1.0 / (double)a.temperature;
+  {  // the decision the residual pass made for this sequence
+    const int R = 2 * a.gamma + 1;
+    if (threadIdx.x < (unsigned)R) {
+      rd.M[threadIdx.x] = L.rmax[(size_t)b * R + threadIdx.x];
+      rd.iZ[threadIdx.x] = L.iz[(size_t)b * R + threadIdx.x];
+    }
+    if (threadIdx.x == 0) rd.n = L.nacc[b];
+    __syncthreads();
+  }
+  const float c_log2 = 1.4426950408889634f / a.temperature;
   const int n = rd.n;
+  const double u = philox_uniform(a.seed, a.offset, b, n, 1);
+
+  // Chunk level: residual mass per chunk (or p's, if the residual has none).
+  double total = 0.0;
+  {
+    double v = 0.0;
+    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads) v += L.wsum[(size_t)b * a.n_chunks + c];
+    total = block_inclusive_scan(v, scan);
+    total = scan[kThreads - 1];
+    __syncthreads();
+  }
+  const bool use_p = !(total > 0.0);
+  const double* cs = (use_p ? L.psum : L.wsum) + (size_t)b * a.n_chunks;
+  if (use_p) {
+    double v = 0.0;
+    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads) v += cs[c];
+    block_inclusive_scan(v, scan);
+    total = scan[kThreads - 1];
+    __syncthreads();
+  }
+  const double target = u * total;
+  // Thread t owns chunks [t*per, (t+1)*per): the first chunk whose running
+  // sum passes the target holds the draw.
+  const int per = (a.n_chunks + kThreads - 1) / kThreads;
+  const int c0 = min(a.n_chunks, (int)threadIdx.x * per), c1 = min(a.n_chunks, c0 + per);
+  double own = 0.0;
+  for (int c = c0; c < c1; ++c) own += cs[c];
+  const double incl = block_inclusive_scan(own, scan);
   if (threadIdx.x == 0) {
-    const double u = philox_uniform(a.seed, a.offset, b, n, 1);
-    const double* cs = L.wsum + (size_t)b * a.n_chunks;
-    double total = 0.0;
-    for (int c = 0; c < a.n_chunks; ++c) total += cs[c];
-    int use_p = 0;
-    if (!(total > 0.0)) {  // the residual has no mass (rounding only): draw from p
-      use_p = 1;
-      cs = L.psum + (size_t)b * a.n_chunks;
-      total = 0.0;
-      for (int c = 0; c < a.n_chunks; ++c) total += cs[c];
-    }
-    const double target = u * total;
-    double cum = 0.0;
-    int chunk = -1, last_pos = 0;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      if (cs[c] > 0.0) last_pos = c;
-      if (chunk < 0 && cum + cs[c] > target) {
-        chunk = c;
-        s_base = cum;
-      }
-      if (chunk < 0) cum += cs[c];
-    }
-    s_fallback = chunk < 0;
-    if (chunk < 0) {
-      chunk = last_pos;
-      s_base = 0.0;
-    }
-    s_chunk = chunk;
-    s_use_p = use_p;
-    s_target = target;
+    s_chunk = 0x7fffffff;
+    s_pos_last = -1;
     s_first = 0x7fffffff;
     s_last = -1;
   }
   __syncthreads();
-  // Ordered scan of the chosen chunk: thread t owns tokens [lo + 16t, lo + 16t + 16).
-  const int lo = s_chunk * kChunk, hi = min(a.V, lo + kChunk);
+  double run = incl - own;
+  for (int c = c0; c < c1; ++c) {
+    if (cs[c] > 0.0) atomicMax(&s_pos_last, c);
+    if (run + cs[c] > target) {
+      atomicMin(&s_chunk, c);
+      break;
+    }
+    run += cs[c];
+  }
+  __syncthreads();
+  const bool fallback = s_chunk == 0x7fffffff;
+  const int chunk = fallback ? max(s_pos_last, 0) : s_chunk;
+  // base = mass of the chunks before `chunk`
+  double before = 0.0;
+  for (int c = c0; c < c1; ++c)
+    if (c < chunk) before += cs[c];
+  block_inclusive_scan(before, scan);
+  const double base = scan[kThreads - 1];
+  __syncthreads();
+
+  // Token level inside the chunk: thread t owns tokens [lo + 16t, lo + 16t + 16).
+  const int lo = chunk * kChunk, hi = min(a.V, lo + kChunk);
   const int t0 = min(hi, lo + kPerThread * (int)threadIdx.x), t1 = min(hi, t0 + kPerThread);
   double w[kPerThread];
   double local = 0.0;
@@ -273,41 +392,31 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(SampleArgs a) {
     w[k] = 0.0;
     if (t0 + k < t1) {
       double p;
-      const double r = draw_weight(a, rd, b, t0 + k, inv_t, &p);
-      w[k] = s_use_p ? p : r;
+      const double r = draw_weight(a, rd, b, t0 + k, c_log2, &p);
+      w[k] = use_p ? p : r;
       local += w[k];
     }
   }
-  scan[threadIdx.x] = local;
-  __syncthreads();
-  if (threadIdx.x == 0) {  // exclusive prefix in token order
-    double run = 0.0;
-    for (int i = 0; i < kThreads; ++i) {
-      const double v = scan[i];
-      scan[i] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  double run = s_base + scan[threadIdx.x];
+  const double tincl = block_inclusive_scan(local, scan);
+  double trun = base + tincl - local;
   int first = 0x7fffffff, last = -1;
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     if (t0 + k < t1) {
       if (w[k] > 0.0) last = t0 + k;
-      run += w[k];
-      if (first == 0x7fffffff && !s_fallback && run > s_target) first = t0 + k;
+      trun += w[k];
+      if (first == 0x7fffffff && !fallback && trun > target) first = t0 + k;
     }
   }
   if (first != 0x7fffffff) atomicMin(&s_first, first);
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x <= (unsigned)a.gamma) {
+    const int i = threadIdx.x;
     const int token = s_first != 0x7fffffff ? s_first : s_last;
-    int32_t* out = a.out_tokens + (size_t)b * (a.gamma + 1);
-    for (int i = 0; i <= a.gamma; ++i)
-      out[i] = i < n ? a.draft_tokens[(size_t)b * a.gamma + i] : (i == n ? token : -1);
-    a.num_accepted[b] = n;
+    a.out_tokens[(size_t)b * (a.gamma + 1) + i] =
+        i < n ? a.draft_tokens[(size_t)b * a.gamma + i] : (i == n ? token : -1);
+    if (i == 0) a.num_accepted[b] = n;
   }
 }
 
@@ -317,7 +426,8 @@ int32_t sample_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
 
 size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab) {
   const size_t C = (size_t)sample_chunks(vocab), R = 2 * (size_t)gamma + 1;
-  return sizeof(double) * B * R * C + 2 * sizeof(double) * B * C + sizeof(float) * B * R * C;
+  return sizeof(double) * B * R * C + 2 * sizeof(double) * B * C + sizeof(double) * B * R +
+         sizeof(float) * B * R * C + sizeof(float) * B * R + sizeof(int) * B;
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {

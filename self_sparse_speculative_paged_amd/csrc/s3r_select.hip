@@ -19,6 +19,7 @@ namespace s3r {
 namespace {
 
 constexpr int kMaxSelectPages = 12288;  // keys staged in LDS by the top-k pass
+constexpr int kSelectPagesPerBlock = 128;  // pages scored by one 256-thread block
 
 // ---------------------------------------------------------------------------
 // Bounds: one wave per (sequence, logical page, kv head). Each lane owns 8
@@ -48,17 +49,39 @@ __global__ __launch_bounds__(64) void bounds_kernel(BoundsArgs a) {
     mn[e] = __builtin_huge_valf();
     mx[e] = -__builtin_huge_valf();
   }
-  for (int t = rg; t < valid; t += kRg) {
-    const T* row = kbase + (size_t)t * kD;
+  // Every row this lane covers is loaded before any is folded (one round trip).
+  constexpr int kRows = kPage / kRg;
+  float v[kRows][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v;
-      if constexpr (sizeof(T) == 2)
-        v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row)[e]);
-      else
-        v = reinterpret_cast<const float*>(row)[e];
-      mn[e] = fminf(mn[e], v);
-      mx[e] = fmaxf(mx[e], v);
+  for (int i = 0; i < kRows; ++i) {
+    const int t = rg + kRg * i;
+    const T* row = kbase + (size_t)(t < valid ? t : 0) * kD;
+    if constexpr (sizeof(T) == 2) {
+      const uint4 raw = load_nt16<uint4>(row);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[i][2 * e] = __uint_as_float(w[e] << 16);
+        v[i][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      const f32x4 lo4 = load_nt16<f32x4>(row);
+      const f32x4 hi4 = load_nt16<f32x4>(row + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[i][e] = lo4[e];
+        v[i][4 + e] = hi4[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    if (rg + kRg * i < valid) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mn[e] = fminf(mn[e], v[i][e]);
+        mx[e] = fmaxf(mx[e], v[i][e]);
+      }
     }
   }
 #pragma unroll
@@ -90,19 +113,25 @@ __global__ __launch_bounds__(64) void bounds_kernel(BoundsArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T, int kD, int kG>
 __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
-  constexpr int kLpp = kD / 8;
-  constexpr int kPpw = 64 / kLpp;
+  constexpr int kLpp = kD / 8;            // lanes per page (8 d per lane)
+  constexpr int kGroups = 256 / kLpp;     // page groups per block
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int seq_len = a.seq_lens[b];
   const int n = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   if (a.k >= n) return;  // every page is taken; the top-k pass writes 0..n-1
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane % kLpp, sub = lane / kLpp;
-  const int per_block = (n + gridDim.y - 1) / gridDim.y;
-  const int start = blockIdx.y * per_block, end = min(n, start + per_block);
+  const int c = threadIdx.x % kLpp, grp = threadIdx.x / kLpp;
+  const int start = blockIdx.y * kSelectPagesPerBlock;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
   float* scores = a.scores + (size_t)bh * a.max_pages;
+  constexpr int kIter = kSelectPagesPerBlock / kGroups;
+  // All page ids first, then all bounds: one dependent round trip per block.
+  int phys[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int j = start + grp + kGroups * i;
+    phys[i] = j < n ? pt[j] : -1;
+  }
 
   if constexpr (sizeof(T) == 2) {
     bf16x2 qp[kG][4], qn[kG][4];
@@ -119,12 +148,20 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
         qn[g][e / 2][e % 2] = neg ? v : z;
       }
     const uint16_t* bb = static_cast<const uint16_t*>(a.bounds);
-    for (int j = start + wave * kPpw + sub; j < end; j += 4 * kPpw) {
-      const uint16_t* pb = bb + ((size_t)pt[j] * a.Hkv + h) * 2 * kD + 8 * c;
-      const uint4 kmin = *reinterpret_cast<const uint4*>(pb);
-      const uint4 kmax = *reinterpret_cast<const uint4*>(pb + kD);
-      const uint32_t mn[4] = {kmin.x, kmin.y, kmin.z, kmin.w};
-      const uint32_t mx[4] = {kmax.x, kmax.y, kmax.z, kmax.w};
+    uint4 kmin[kIter], kmax[kIter];
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const uint16_t* pb = bb + ((size_t)(phys[i] < 0 ? 0 : phys[i]) * a.Hkv + h) * 2 * kD + 8 * c;
+      if (phys[i] >= 0) {
+        kmin[i] = load_nt16<uint4>(pb);
+        kmax[i] = load_nt16<uint4>(pb + kD);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      if (phys[i] < 0) continue;  // uniform within the page group
+      const uint32_t mn[4] = {kmin[i].x, kmin[i].y, kmin[i].z, kmin[i].w};
+      const uint32_t mx[4] = {kmax[i].x, kmax[i].y, kmax[i].z, kmax[i].w};
       float best = -__builtin_huge_valf();
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -134,11 +171,9 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
           acc = __builtin_amdgcn_fdot2_f32_bf16(qp[g][p], __builtin_bit_cast(bf16x2, mx[p]), acc, false);
           acc = __builtin_amdgcn_fdot2_f32_bf16(qn[g][p], __builtin_bit_cast(bf16x2, mn[p]), acc, false);
         }
-#pragma unroll
-        for (int x = 1; x < kLpp; x <<= 1) acc += __shfl_xor(acc, x, 64);
-        best = fmaxf(best, acc);
+        best = fmaxf(best, group_sum<kLpp>(acc));
       }
-      if (c == 0) scores[j] = best * a.scale;
+      if (c == 0) scores[start + grp + kGroups * i] = best * a.scale;
     }
   } else {
     float qp[kG][8], qn[kG][8];
@@ -152,8 +187,10 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
         qn[g][e] = v < 0.f ? v : 0.f;
       }
     const float* bb = static_cast<const float*>(a.bounds);
-    for (int j = start + wave * kPpw + sub; j < end; j += 4 * kPpw) {
-      const float* pb = bb + ((size_t)pt[j] * a.Hkv + h) * 2 * kD + 8 * c;
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      if (phys[i] < 0) continue;
+      const float* pb = bb + ((size_t)phys[i] * a.Hkv + h) * 2 * kD + 8 * c;
       float mn[8], mx[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -169,18 +206,16 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
           acc = fmaf(qp[g][e], mx[e], acc);
           acc = fmaf(qn[g][e], mn[e], acc);
         }
-#pragma unroll
-        for (int x = 1; x < kLpp; x <<= 1) acc += __shfl_xor(acc, x, 64);
-        best = fmaxf(best, acc);
+        best = fmaxf(best, group_sum<kLpp>(acc));
       }
-      if (c == 0) scores[j] = best * a.scale;
+      if (c == 0) scores[start + grp + kGroups * i] = best * a.scale;
     }
   }
 }
 
-// Exclusive prefix sum over the 256 threads of a block (fixed order).
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
-                                                         uint32_t* total) {
+// Exclusive prefix sum over the threads of a block (fixed order).
+template <int kThreadsPerBlock>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t incl = v;
 #pragma unroll
@@ -192,7 +227,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   __syncthreads();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  if (total) *total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
   __syncthreads();
   return base + incl - v;
 }
@@ -205,16 +239,23 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: exact radix select of the k-th largest key (8 bits per pass), then a
-// stable compaction in page order, which emits the kept pages ascending. Ties
-// on the threshold key keep the lowest page indices.
+// Top-k: exact radix select of the k-th largest key, then a stable compaction
+// in page order, which emits the kept pages ascending. Ties on the threshold
+// key keep the lowest page indices. Key bits shared by every key (the common
+// prefix of the block's min and max key) are skipped; the rest are resolved
+// 9 bits per pass.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
+constexpr int kTopkThreads = 1024;
+constexpr int kDigitBits = 9;
+constexpr int kBins = 1 << kDigitBits;
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_tot[4];
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wave_tot[kTopkThreads / 64];
+  __shared__ uint32_t s_min[kTopkThreads / 64], s_max[kTopkThreads / 64];
   __shared__ uint32_t s_digit, s_krem;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int seq_len = a.seq_lens[b];
@@ -223,50 +264,105 @@ __global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
   int32_t* out = a.selected + (size_t)bh * k;
   if (h == 0 && tid == 0) a.num_selected[b] = min(k, n);
   if (k >= n) {
-    for (int t = tid; t < k; t += 256) out[t] = t < n ? t : -1;
+    for (int t = tid; t < k; t += kTopkThreads) out[t] = t < n ? t : -1;
     return;
   }
   const float* sc = a.scores + (size_t)bh * a.max_pages;
-  for (int j = tid; j < n; j += 256) keys[j] = order_key(sc[j]);
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  // Scores are loaded 8 per thread at a time, all in flight together.
+  for (int j0 = 0; j0 < n; j0 += 8 * kTopkThreads) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + tid + kTopkThreads * e;
+      v[e] = j < n ? sc[j] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + tid + kTopkThreads * e;
+      if (j < n) {
+        const uint32_t key = order_key(v[e]);
+        keys[j] = key;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+  }
+  for (int x = 32; x >= 1; x >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, x, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, x, 64));
+  }
+  if (lane == 0) {
+    s_min[wave] = kmin;
+    s_max[wave] = kmax;
+  }
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
   __syncthreads();
-
-  uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += 256) {
-      const uint32_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    kmin = min(kmin, s_min[w]);
+    kmax = max(kmax, s_max[w]);
+  }
+  const int varying = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));
+  uint32_t prefix = kmin & (varying >= 32 ? 0u : ~((1u << varying) - 1u));
+  uint32_t mask = varying >= 32 ? 0u : ~((1u << varying) - 1u);
+  uint32_t krem = (uint32_t)k;
+  for (int lo_bit = varying - kDigitBits; lo_bit > -kDigitBits; lo_bit -= kDigitBits) {
+    const int shift = max(lo_bit, 0);
+    const int width = lo_bit >= 0 ? kDigitBits : kDigitBits + lo_bit;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
+      const int j = j0 + tid;
+      const uint32_t key = j < n ? keys[j] : 0u;
+      if (j < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    // Counts of digits from the top: thread t holds digit 255 - t.
-    const uint32_t cnt = hist[255 - tid];
-    const uint32_t above = block_exclusive_scan(cnt, wave_tot, nullptr);
-    if (above < krem && above + cnt >= krem) {
-      s_digit = 255u - tid;
-      s_krem = krem - above;
+    if (wave == 0) {
+      // Lane l holds the 8 bins 8l..8l+7 counted from the top digit down.
+      constexpr int kPer = kBins / 64;
+      uint32_t cnt[kPer], own = 0;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        cnt[e] = hist[kBins - 1 - (kPer * lane + e)];
+        own += cnt[e];
+      }
+      uint32_t incl = own;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+      }
+      uint32_t above = incl - own;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        if (above < krem && above + cnt[e] >= krem) {
+          s_digit = (uint32_t)(kBins - 1 - (kPer * lane + e));
+          s_krem = krem - above;
+        }
+        above += cnt[e];
+      }
     }
     __syncthreads();
     prefix |= s_digit << shift;
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     krem = s_krem;
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
   }
   const uint32_t thr = prefix;
 
   // Contiguous chunk per thread, scanned twice: equal-key ranks, then output slots.
-  const int chunk = (n + 255) / 256;
+  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
   const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
   uint32_t n_eq = 0;
   for (int j = lo; j < hi; ++j) n_eq += keys[j] == thr;
-  const uint32_t eq_before = block_exclusive_scan(n_eq, wave_tot, nullptr);
+  const uint32_t eq_before = block_exclusive_scan<kTopkThreads>(n_eq, wave_tot);
   uint32_t n_take = 0, eq_rank = eq_before;
   for (int j = lo; j < hi; ++j) {
     const uint32_t key = keys[j];
     if (key > thr) ++n_take;
     else if (key == thr) n_take += (eq_rank++ < krem);
   }
-  const uint32_t slot0 = block_exclusive_scan(n_take, wave_tot, nullptr);
+  const uint32_t slot0 = block_exclusive_scan<kTopkThreads>(n_take, wave_tot);
   uint32_t slot = slot0;
   eq_rank = eq_before;
   for (int j = lo; j < hi; ++j) {
@@ -314,8 +410,7 @@ hipError_t launch_bounds(const BoundsArgs& a, s3r_dtype dt, hipStream_t stream) 
 }
 
 hipError_t launch_select(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) {
-  // ~128 pages per 256-thread block; at least one block per (sequence, head).
-  const int ychunks = max(1, (a.max_pages + 127) / 128);
+  const int ychunks = max(1, (a.max_pages + kSelectPagesPerBlock - 1) / kSelectPagesPerBlock);
   const dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)ychunks);
   hipError_t e;
   if (dt == S3R_BF16)
@@ -324,7 +419,7 @@ hipError_t launch_select(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) 
     e = a.D == 128 ? launch_score<float, 128>(a, grid, stream) : launch_score<float, 64>(a, grid, stream);
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)a.max_pages * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(kTopkThreads), lds, stream, a);
   return hipGetLastError();
 }
 

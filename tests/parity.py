@@ -30,7 +30,13 @@ def check_pages(gpu_sel, gpu_nsel, ref_sel, ref_nsel, ref_scores, k, tie=1e-4):
 
 
 def check_tokens(gpu_out, gpu_n, ref_out, ref_n, decisions, window=1e-6):
-    """Returns the number of sequences compared in full."""
+    """Compare a round's tokens; returns the number of sequences compared in full.
+
+    Decisions before the first one within `window` of its threshold are
+    compared exactly. If that first close decision is the round's final draw,
+    the accepted count and every accepted draft are still compared; if it is
+    an accept test at slot i, tokens before slot i are compared.
+    """
     full = 0
     for b in range(len(ref_n)):
         close = [d for d in decisions[b] if d[2] <= window]
@@ -39,6 +45,8 @@ def check_tokens(gpu_out, gpu_n, ref_out, ref_n, decisions, window=1e-6):
             assert np.array_equal(gpu_out[b], ref_out[b]), (b, gpu_out[b], ref_out[b])
             full += 1
             continue
-        slot = close[0][0]
+        slot, kind, _ = close[0]
+        if kind == "draw":
+            assert int(gpu_n[b]) == int(ref_n[b]), (b, gpu_n[b], ref_n[b])
         assert np.array_equal(gpu_out[b, :slot], ref_out[b, :slot]), b
     return full
