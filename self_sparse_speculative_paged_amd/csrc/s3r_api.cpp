@@ -54,9 +54,9 @@ s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* s
   a.q = q;
   a.sel = sel;
   a.out = out;
-  const size_t items = (size_t)kv->num_seqs * kv->num_kv_heads * plan.n_splits;
+  const size_t items = (size_t)kv->num_seqs * kv->num_kv_heads * plan.n_groups;
   a.part_o = static_cast<float*>(ws);
-  a.part_ml = a.part_o + items * plan.rows * kv->head_dim;
+  a.part_ml = ws ? a.part_o + items * plan.rows * kv->head_dim : nullptr;
   a.B = kv->num_seqs;
   a.Hq = kv->num_q_heads;
   a.Hkv = kv->num_kv_heads;
@@ -68,6 +68,9 @@ s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* s
   a.rows = plan.rows;
   a.pages_per_split = plan.pages_per_split;
   a.n_splits = plan.n_splits;
+  a.waves_per_group = plan.waves_per_group;
+  a.n_groups = plan.n_groups;
+  a.lds_region_bytes = plan.lds_region_bytes;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_bf16 = out_dtype == S3R_BF16;
   return from_hip(s3r::launch_attention(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));

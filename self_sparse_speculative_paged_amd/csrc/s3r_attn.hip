@@ -69,8 +69,8 @@ template <int kD, int kNB>
 __device__ __forceinline__ void write_partial(const AttnArgs& a, int b, int h, int split,
                                               const float (&m_run)[kNB], float (&l_run)[kNB],
                                               const f32x4 (&acc)[kNB][kD / 16]) {
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-  const size_t item = ((size_t)b * a.Hkv + h) * a.n_splits + split;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const size_t item = ((size_t)b * a.Hkv + h) * a.n_groups + split;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const float l = wave_xor_sum<16, 32>(l_run[nb]);
@@ -87,6 +87,49 @@ __device__ __forceinline__ void write_partial(const AttnArgs& a, int b, int h, i
   }
 }
 
+// Merges the kW per-wave partials of one workgroup (LDS regions of
+// a.lds_region_bytes each, laid out o[rows][D] then ml[rows][2]) and writes the
+// final rows, or one group partial when the (sequence, head) spans several
+// workgroups.
+template <int kD, int kW>
+__device__ __forceinline__ void merge_group(const AttnArgs& a, int b, int h, int group,
+                                            const char* lds) {
+  const int R = a.rows;
+  for (int idx = threadIdx.x; idx < R * kD; idx += 64 * kW) {
+    const int row = idx / kD, d = idx % kD;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kW; ++w)
+      M = fmaxf(M, reinterpret_cast<const float*>(lds + (size_t)w * a.lds_region_bytes)[R * kD + 2 * row]);
+    float den = 0.f, o = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const float* po = reinterpret_cast<const float*>(lds + (size_t)w * a.lds_region_bytes);
+        const float c = __builtin_amdgcn_exp2f(po[R * kD + 2 * row] - M);
+        den += c * po[R * kD + 2 * row + 1];
+        o += c * po[row * kD + d];
+      }
+    }
+    if (a.n_groups == 1) {
+      const int gl = row / a.nq, i = row % a.nq;
+      const size_t oi = (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + d;
+      const float v = den > 0.f ? o / den : 0.f;
+      if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(v);
+      else
+        static_cast<float*>(a.out)[oi] = v;
+    } else {
+      const size_t item = ((size_t)b * a.Hkv + h) * a.n_groups + group;
+      a.part_o[(item * R + row) * kD + d] = o;
+      if (d == 0) {
+        a.part_ml[(item * R + row) * 2] = M;
+        a.part_ml[(item * R + row) * 2 + 1] = den;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 KV
 // ---------------------------------------------------------------------------
@@ -94,26 +137,27 @@ template <int kD, int kNB>
 struct Bf16Tile {
   bf16x8 k[2][kD / 32];  // A operand of S^T for the two 16-token M-blocks
   bf16x8 v[kD / 16];     // A operand of O^T for each 16-wide d block
+  WindowPages w;         // the window's pages
 };
 
 template <int kD, int kNB>
 __device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint16_t* kp,
-                                               const uint16_t* vp, int Hkv, int h,
-                                               const WindowPages& w) {
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+                                               const uint16_t* vp, int Hkv, int h) {
+  const WindowPages w = t.w;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   // M-block mb, row m = l16 holds window token 8*(m/4) + 4*mb + m%4: tokens
   // 0..15 come from page A (l16 < 8), 16..31 from page B.
   const int kphys = (l16 >= 8) ? w.physB : w.physA;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int slot = (8 * (l16 >> 2) + 4 * mb + (l16 & 3)) & 15;
-    const uint16_t* base =
-        kp + (((size_t)kphys * Hkv + h) * kPage + slot) * kD + (kD / 4) * g4;
+    const uint16_t* base = kp + (((size_t)kphys * Hkv + h) * kPage + slot) * kD + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < kD / 32; ++s) t.k[mb][s] = *reinterpret_cast<const bf16x8*>(base + 8 * s);
+    for (int s = 0; s < kD / 32; ++s) t.k[mb][s] = *reinterpret_cast<const bf16x8*>(base + 32 * s);
   }
-  // K loads cover 64 of each row's 256 bytes per instruction, so they stay
-  // cached: the four k-step loads of a row share its two 128-byte lines.
+  // Contraction index (k-step s, lane group g4, element e) <-> d = 32 s + 8 g4 + e,
+  // the same for K and Q: one K load instruction reads 64 contiguous bytes of
+  // each of 16 token rows. K loads stay cached: two instructions share a line.
   // O^T A operand: lane holds V^T[d = 16*mb + l16][window tokens 8*g4 .. 8*g4+7];
   // each load instruction covers two whole 512-byte runs, streamed (nontemporal).
   const int vphys = (g4 >= 2) ? w.physB : w.physA;
@@ -126,11 +170,14 @@ __device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint1
 template <int kD, int kNB>
 __device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
                                                   const bf16x8 (&qb)[kNB][kD / 32],
-                                                  const int (&qpos)[kNB], const WindowPages& w,
-                                                  bool need_mask, float scale_log2,
-                                                  float (&m_run)[kNB], float (&l_run)[kNB],
-                                                  f32x4 (&acc)[kNB][kD / 16]) {
-  const int lane = threadIdx.x, g4 = lane >> 4;
+                                                  const int (&qpos)[kNB], int min_qpos,
+                                                  float scale_log2, float (&m_run)[kNB],
+                                                  float (&l_run)[kNB], f32x4 (&acc)[kNB][kD / 16]) {
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const WindowPages w = t.w;
+  // Only windows reaching past the first query's position, or holding an
+  // invalid page, need the mask.
+  const bool need_mask = w.lpA < 0 || w.lpB < 0 || 16 * max(w.lpA, w.lpB) + 15 > min_qpos;
   f32x4 sacc[2][kNB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -184,45 +231,30 @@ constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : 2); }
 template <int kNB>
 constexpr int bf16_waves_per_simd() { return kNB == 1 ? 2 : 1; }
 
-template <int kD, int kNB, bool kSparse>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(bf16_waves_per_simd<kNB>(), 8)))
+// Each wave of a kW-wave workgroup owns one split of the same (sequence, kv
+// head). Its LDS region holds first its window table, then (once its pipeline
+// has drained) its (m, l, o) partial; after a barrier the workgroup merges the
+// kW partials and writes either the final output (one group per (sequence,
+// head)) or one group partial for the global combine.
+template <int kD, int kNB, bool kSparse, int kW>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(bf16_waves_per_simd<kNB>(), 8)))
 void attn_bf16_kernel(AttnArgs a) {
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-  const int split = blockIdx.x % a.n_splits;
-  const int bh = blockIdx.x / a.n_splits;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int wave = kW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = blockIdx.x % a.n_groups;
+  const int bh = blockIdx.x / a.n_groups;
   const int h = bh % a.Hkv, b = bh / a.Hkv;
   const int seq_len = a.seq_lens[b];
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
-  const int j0 = split * a.pages_per_split;
-  if (j0 >= n_items) return;
+  const int g0 = group * kW * a.pages_per_split;
+  if (g0 >= n_items && a.n_groups > 1) return;  // the global combine skips this group
+  const int j0 = g0 + wave * a.pages_per_split;
   const int j1 = min(j0 + a.pages_per_split, n_items);
+  const bool active = j0 < n_items;
 
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
-  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  const int32_t* sel = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-
-  bf16x8 qb[kNB][kD / 32];
-  int qpos[kNB];
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int row = 16 * nb + l16;
-    if (row < a.rows) {
-      const int gl = row / a.nq, i = row % a.nq;
-      const uint16_t* qrow =
-          qg + (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + (kD / 4) * g4;
-#pragma unroll
-      for (int s = 0; s < kD / 32; ++s) qb[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
-      qpos[nb] = seq_len - a.nq + i;
-    } else {
-#pragma unroll
-      for (int s = 0; s < kD / 32; ++s) qb[nb][s] = bf16x8{};
-      qpos[nb] = -1;
-    }
-  }
-
+  extern __shared__ int4 lds[];
+  char* region = reinterpret_cast<char*>(lds) + (size_t)wave * a.lds_region_bytes;
   float m_run[kNB], l_run[kNB];
   f32x4 acc[kNB][kD / 16];
 #pragma unroll
@@ -233,69 +265,107 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int mb = 0; mb < kD / 16; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int min_qpos = seq_len - a.nq;
-  // Resolve every window's pages once: lanes look up the item's page ids in
-  // parallel (selection entry, then page table) into an LDS table, so the
-  // pipeline below never waits on a dependent page-table load.
-  extern __shared__ int4 win_tab[];  // per window {lpA, lpB, physA, physB}
-  const int n_win = (j1 - j0 + 1) / 2;
-  {
-    const int fallback = pt[0];
-    for (int w0 = 0; w0 < n_win; w0 += 64) {
-      const int wi = w0 + lane;
-      if (wi < n_win) {
-        const int jj = j0 + 2 * wi;
-        int4 e;
-        e.x = logical_page<kSparse>(sel, jj, n_pages);
-        e.y = (jj + 1 < j1) ? logical_page<kSparse>(sel, jj + 1, n_pages) : -1;
-        e.z = e.x >= 0 ? pt[e.x] : fallback;
-        e.w = e.y >= 0 ? pt[e.y] : e.z;
-        win_tab[wi] = e;
-      }
-    }
-  }
-  auto pages_of = [&](int wi) {
-    const int4 e = win_tab[wi];
-    WindowPages w;
-    w.lpA = __builtin_amdgcn_readfirstlane(e.x);
-    w.lpB = __builtin_amdgcn_readfirstlane(e.y);
-    w.physA = __builtin_amdgcn_readfirstlane(e.z);
-    w.physB = __builtin_amdgcn_readfirstlane(e.w);
-    return w;
-  };
-  auto masked = [&](const WindowPages& w) {
-    return w.lpA < 0 || w.lpB < 0 || 16 * max(w.lpA, w.lpB) + 15 > min_qpos;
-  };
+  if (active) {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
+    const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+    const int32_t* sel = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q);
 
-  // kStages-deep register pipeline: while window i is computed, the loads of
-  // windows i+1 .. i+kStages-1 are in flight. Three stages fit the 512
-  // registers of a single wave per SIMD up to two row blocks.
-  constexpr int kStages = bf16_stages<kNB>();
-  Bf16Tile<kD, kNB> t[kStages];
-  WindowPages w[kStages];
+    bf16x8 qb[kNB][kD / 32];
+    int qpos[kNB];
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (s < n_win) {
-      w[s] = pages_of(s);
-      load_bf16_tile<kD, kNB>(t[s], kp, vp, a.Hkv, h, w[s]);
-    }
-  }
-  for (int base = 0; base < n_win; base += kStages) {
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int row = 16 * nb + l16;
+      if (row < a.rows) {
+        const int gl = row / a.nq, i = row % a.nq;
+        const uint16_t* qrow = qg + (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < kStages; ++s) {
-      const int i = base + s;
-      if (i >= n_win) break;
-      const int ip = i + kStages - 1;
-      if (ip < n_win) {
-        w[(s + kStages - 1) % kStages] = pages_of(ip);
-        load_bf16_tile<kD, kNB>(t[(s + kStages - 1) % kStages], kp, vp, a.Hkv, h,
-                                w[(s + kStages - 1) % kStages]);
+        for (int s = 0; s < kD / 32; ++s) qb[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+        qpos[nb] = seq_len - a.nq + i;
+      } else {
+#pragma unroll
+        for (int s = 0; s < kD / 32; ++s) qb[nb][s] = bf16x8{};
+        qpos[nb] = -1;
       }
-      compute_bf16_tile<kD, kNB>(t[s], qb, qpos, w[s], masked(w[s]), a.scale_log2, m_run, l_run,
-                                 acc);
+    }
+
+    const int min_qpos = seq_len - a.nq;
+    // Resolve every window's pages once: lanes look up the split's page ids in
+    // parallel (selection entry, then page table) into this wave's LDS table,
+    // so the pipeline below never waits on a dependent page-table load.
+    int4* win_tab = reinterpret_cast<int4*>(region);  // per window {lpA, lpB, physA, physB}
+    const int n_win = (j1 - j0 + 1) / 2;
+    {
+      const int fallback = pt[0];
+      for (int w0 = 0; w0 < n_win; w0 += 64) {
+        const int wi = w0 + lane;
+        if (wi < n_win) {
+          const int jj = j0 + 2 * wi;
+          int4 e;
+          e.x = logical_page<kSparse>(sel, jj, n_pages);
+          e.y = (jj + 1 < j1) ? logical_page<kSparse>(sel, jj + 1, n_pages) : -1;
+          e.z = e.x >= 0 ? pt[e.x] : fallback;
+          e.w = e.y >= 0 ? pt[e.y] : e.z;
+          win_tab[wi] = e;
+        }
+      }
+    }
+    auto pages_of = [&](int wi) {
+      const int4 e = win_tab[wi];
+      WindowPages w;
+      w.lpA = __builtin_amdgcn_readfirstlane(e.x);
+      w.lpB = __builtin_amdgcn_readfirstlane(e.y);
+      w.physA = __builtin_amdgcn_readfirstlane(e.z);
+      w.physB = __builtin_amdgcn_readfirstlane(e.w);
+      return w;
+    };
+    // kStages-deep register pipeline: while window i is computed, the loads of
+    // windows i+1 .. i+kStages-1 are in flight. Three stages fit the 512
+    // registers of a single wave per SIMD up to two row blocks.
+    constexpr int kStages = bf16_stages<kNB>();
+    Bf16Tile<kD, kNB> t[kStages];
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) {
+      if (s < n_win) {
+        t[s].w = pages_of(s);
+        load_bf16_tile<kD, kNB>(t[s], kp, vp, a.Hkv, h);
+      }
+    }
+    for (int base = 0; base < n_win; base += kStages) {
+#pragma unroll
+      for (int s = 0; s < kStages; ++s) {
+        const int i = base + s;
+        if (i >= n_win) break;
+        const int ip = i + kStages - 1;
+        if (ip < n_win) {
+          t[(s + kStages - 1) % kStages].w = pages_of(ip);
+          load_bf16_tile<kD, kNB>(t[(s + kStages - 1) % kStages], kp, vp, a.Hkv, h);
+        }
+        compute_bf16_tile<kD, kNB>(t[s], qb, qpos, min_qpos, a.scale_log2, m_run, l_run, acc);
+      }
     }
   }
-  write_partial<kD, kNB>(a, b, h, split, m_run, l_run, acc);
+  // This wave's partial into its LDS region: o[rows][D], then ml[rows][2]
+  // (o first keeps its 16-byte stores aligned for any row count).
+  float* po = reinterpret_cast<float*>(region);
+  float* pml = po + a.rows * kD;
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const float l = wave_xor_sum<16, 32>(l_run[nb]);
+    const int row = 16 * nb + l16;
+    if (row < a.rows) {
+      if (g4 == 0) {
+        pml[2 * row] = m_run[nb];
+        pml[2 * row + 1] = l;
+      }
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb)
+        *reinterpret_cast<f32x4*>(po + row * kD + 16 * mb + 4 * g4) = acc[nb][mb];
+    }
+  }
+  if constexpr (kW > 1) __syncthreads();
+  merge_group<kD, kW>(a, b, h, group, reinterpret_cast<const char*>(lds));
 }
 
 // ---------------------------------------------------------------------------
@@ -310,7 +380,7 @@ struct F32Tile {
 template <int kD>
 __device__ __forceinline__ void load_f32_tile(F32Tile<kD>& t, const float* kp, const float* vp,
                                               int Hkv, int h, int phys) {
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const float* kb = kp + (((size_t)phys * Hkv + h) * kPage + l16) * kD + (kD / 4) * g4;
 #pragma unroll
   for (int s = 0; s < kD / 16; ++s) {
@@ -326,9 +396,9 @@ __device__ __forceinline__ void load_f32_tile(F32Tile<kD>& t, const float* kp, c
 
 template <int kD, int kNB, bool kSparse>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-  const int split = blockIdx.x % a.n_splits;
-  const int bh = blockIdx.x / a.n_splits;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x % a.n_groups;
+  const int bh = blockIdx.x / a.n_groups;
   const int h = bh % a.Hkv, b = bh / a.Hkv;
   const int seq_len = a.seq_lens[b];
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
@@ -421,8 +491,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const int seq_len = a.seq_lens[b];
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
-  const int ns = (n_items + a.pages_per_split - 1) / a.pages_per_split;
-  const size_t item0 = ((size_t)b * a.Hkv + h) * a.n_splits;
+  const int per_group = a.pages_per_split * a.waves_per_group;
+  const int ns = (n_items + per_group - 1) / per_group;
+  const size_t item0 = ((size_t)b * a.Hkv + h) * a.n_groups;
 
   // Splits are folded 8 at a time with all their loads in flight together.
   constexpr int kBatch = 8;
@@ -470,15 +541,27 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 
 template <int kD, int kNB, bool kSparse>
 hipError_t launch_typed(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
-  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_splits));
+  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_groups));
   if (dt == S3R_BF16) {
-    const size_t lds = sizeof(int4) * (size_t)((a.pages_per_split + 1) / 2);
-    hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse>), grid, dim3(64), lds, stream, a);
-  }
-  else
+    const size_t lds = (size_t)a.lds_region_bytes * a.waves_per_group;
+    switch (a.waves_per_group) {
+      case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse, 1>), grid, dim3(64), lds, stream, a); break;
+      case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse, 2>), grid, dim3(128), lds, stream, a); break;
+      case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse, 4>), grid, dim3(256), lds, stream, a); break;
+      case 8:
+        if constexpr (bf16_waves_per_simd<kNB>() >= 2) {
+          hipLaunchKernelGGL((attn_bf16_kernel<kD, kNB, kSparse, 8>), grid, dim3(512), lds, stream, a);
+          break;
+        }
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
     hipLaunchKernelGGL((attn_f32_kernel<kD, kNB, kSparse>), grid, dim3(64), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dt == S3R_BF16 && a.n_groups == 1) return hipSuccess;  // merged in the workgroup
   hipLaunchKernelGGL((attn_combine_kernel<kD, kSparse>), dim3((unsigned)((size_t)a.B * a.nq * a.Hq)),
                      dim3(64), 0, stream, a);
   return hipGetLastError();
@@ -498,10 +581,11 @@ hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
 }  // namespace
 
 SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items) {
-  // As many items as resident waves: 256 CUs x 4 SIMDs x (2 waves per SIMD for
-  // one MFMA row block, 1 otherwise).
+  // As many splits as resident waves: 256 CUs x 4 SIMDs x (2 waves per SIMD
+  // for one MFMA row block, 1 otherwise).
   constexpr long kMinPagesPerSplit = 16;
-  constexpr long kMaxPagesPerSplit = 4096;  // LDS window table <= 32 KB
+  constexpr long kMaxPagesPerSplit = 4096;   // LDS window table <= 32 KB
+  constexpr size_t kMaxGroupLds = 64 * 1024;
   SplitPlan p{};
   const long B = kv.num_seqs, Hkv = kv.num_kv_heads;
   const int G = kv.num_q_heads / kv.num_kv_heads;
@@ -521,8 +605,23 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   p.pages_per_split = (int32_t)pps;
   p.n_splits = (int32_t)((max_items + pps - 1) / pps);
-  const size_t items = (size_t)B * Hkv * p.n_splits;
-  p.workspace_bytes = items * p.rows * ((size_t)kv.head_dim + 2) * sizeof(float);
+  // bf16: the splits of one (sequence, kv head) run as the waves of one
+  // workgroup and are merged in LDS; each wave's region holds its window table,
+  // then its partial.
+  const size_t table = sizeof(int) * 4 * (size_t)((pps + 1) / 2);
+  const size_t partial = sizeof(float) * (size_t)p.rows * (kv.head_dim + 2);
+  p.lds_region_bytes = (int32_t)(((table > partial ? table : partial) + 15) & ~(size_t)15);
+  int w = 1;
+  if (kv.kv_dtype == S3R_BF16) {
+    const int wmax = p.row_blocks == 1 ? 8 : 4;
+    while (w < wmax && w < p.n_splits) w *= 2;
+    while (w > 1 && (size_t)w * p.lds_region_bytes > kMaxGroupLds) w /= 2;
+  }
+  p.waves_per_group = w;
+  p.n_groups = (p.n_splits + w - 1) / w;
+  const bool global_combine = kv.kv_dtype != S3R_BF16 || p.n_groups > 1;
+  const size_t items = (size_t)B * Hkv * p.n_groups;
+  p.workspace_bytes = global_combine ? items * p.rows * ((size_t)kv.head_dim + 2) * sizeof(float) : 0;
   return p;
 }
 

@@ -16,9 +16,12 @@ namespace s3r {
 struct SplitPlan {
   int32_t pages_per_split;
   int32_t n_splits;
-  int32_t rows;       // G * n_queries attention rows per kv head
-  int32_t row_blocks; // ceil(rows / 16): MFMA N-blocks
-  size_t workspace_bytes;
+  int32_t rows;             // G * n_queries attention rows per kv head
+  int32_t row_blocks;       // ceil(rows / 16): MFMA N-blocks
+  int32_t waves_per_group;  // splits merged inside one workgroup (bf16)
+  int32_t n_groups;         // workgroups per (sequence, kv head)
+  int32_t lds_region_bytes; // per-wave LDS region (window table, then partial)
+  size_t workspace_bytes;   // global partials: only when n_groups > 1 (or fp32)
 };
 
 SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items);
@@ -31,10 +34,11 @@ struct AttnArgs {
   const void* q;          // [B][nq][Hq][D]
   const int32_t* sel;     // [B][Hkv][ksel] or nullptr (dense)
   void* out;              // [B][nq][Hq][D]
-  float* part_o;          // [items][rows][D]
-  float* part_ml;         // [items][rows][2] (running max in log2 units, sum)
+  float* part_o;          // [B][Hkv][n_groups][rows][D]
+  float* part_ml;         // [B][Hkv][n_groups][rows][2] (max in log2 units, sum)
   int32_t B, Hq, Hkv, G, D, max_pages, nq, ksel;
   int32_t rows, pages_per_split, n_splits;
+  int32_t waves_per_group, n_groups, lds_region_bytes;
   float scale_log2;       // softmax_scale * log2(e)
   int32_t out_bf16;
 };

@@ -9,12 +9,12 @@
 // first rejection draw from norm(max(0, p_i - q_i)); if all gamma drafts are
 // accepted draw a bonus token from p_gamma.
 //
-// Three passes, all deterministic (fixed-order reductions, no float atomics):
+// Four passes, all deterministic (fixed-order reductions, no float atomics):
 //   stats:    per (sequence, row, 4096-token chunk) max and sum of exp, the sum
 //             accumulated in fp64;
-//   residual: per (sequence, chunk) every block folds the row statistics, runs
-//             the accept scan (identically in every block) and sums its chunk
-//             of the residual (or bonus) weights in fp64;
+//   decide:   per sequence, fold the row statistics and run the accept scan;
+//   residual: per (sequence, chunk) sum the chunk's residual (or bonus)
+//             weights in fp64;
 //   finalize: per sequence, locate the chunk holding u * sum(w), then the token
 //             inside it by an ordered block scan; write the round's tokens.
 // Uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) at key
@@ -238,25 +238,37 @@ __device__ void round_decision(const SampleArgs& a, int b, Round& rd) {
   __syncthreads();
 }
 
-// Weight of token t for the draw at slot n: max(0, p_n - q_n) on a rejection,
-// p_gamma for the bonus. `p_out` receives p (the fallback when the residual
-// has no mass).
-__device__ __forceinline__ double draw_weight(const SampleArgs& a, const Round& rd, int b, int t,
-                                              float c_log2, double* p_out) {
-  const int n = rd.n;
-  const int tr = a.gamma + n;
-  const double p = (double)scaled_exp(row_ptr(a, b, tr)[t], rd.M[tr], c_log2) * rd.iZ[tr];
-  *p_out = p;
-  if (n == a.gamma) return p;
-  const double q = (double)scaled_exp(row_ptr(a, b, n)[t], rd.M[n], c_log2) * rd.iZ[n];
-  return p > q ? p - q : 0.0;
+// One block per sequence: fold the row statistics, run the accept scan and
+// store (row max, 1/normaliser, accepted count) for the two passes that follow.
+__global__ __launch_bounds__(kThreads) void decide_kernel(SampleArgs a) {
+  __shared__ Round rd;
+  const int b = blockIdx.x;
+  round_decision(a, b, rd);
+  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
+  const int R = 2 * a.gamma + 1;
+  if (threadIdx.x < (unsigned)R) {
+    L.rmax[(size_t)b * R + threadIdx.x] = rd.M[threadIdx.x];
+    L.iz[(size_t)b * R + threadIdx.x] = rd.iZ[threadIdx.x];
+  }
+  if (threadIdx.x == 0) L.nacc[b] = rd.n;
+}
+
+__device__ __forceinline__ void load_decision(const SampleArgs& a, int b, Round& rd) {
+  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
+  const int R = 2 * a.gamma + 1;
+  if (threadIdx.x < (unsigned)R) {
+    rd.M[threadIdx.x] = L.rmax[(size_t)b * R + threadIdx.x];
+    rd.iZ[threadIdx.x] = L.iz[(size_t)b * R + threadIdx.x];
+  }
+  if (threadIdx.x == 0) rd.n = L.nacc[b];
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
   __shared__ Round rd;
   __shared__ double redd[4];
   const int c = blockIdx.x, b = blockIdx.y;
-  round_decision(a, b, rd);
+  load_decision(a, b, rd);
   const float c_log2 = 1.4426950408889634f / a.temperature;
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   // All of this thread's logits are loaded before any is used.
@@ -286,137 +298,127 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
     L.wsum[(size_t)b * a.n_chunks + c] = w;
     L.psum[(size_t)b * a.n_chunks + c] = ps;
   }
-  if (c == 0) {  // the finalize pass reuses this block's decision
-    const int R = 2 * a.gamma + 1;
-    if (threadIdx.x < (unsigned)R) {
-      L.rmax[(size_t)b * R + threadIdx.x] = rd.M[threadIdx.x];
-      L.iz[(size_t)b * R + threadIdx.x] = rd.iZ[threadIdx.x];
-    }
-    if (threadIdx.x == 0) L.nacc[b] = rd.n;
-  }
 }
 
-// Inclusive prefix sum of one double per thread over the block, in thread
-// order (Hillis-Steele in LDS; the addition order is fixed).
-__device__ double block_inclusive_scan(double v, double* buf) {
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  for (int d = 1; d < kThreads; d <<= 1) {
-    const double y = threadIdx.x >= (unsigned)d ? buf[threadIdx.x - d] : 0.0;
-    __syncthreads();
-    buf[threadIdx.x] += y;
-    __syncthreads();
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(v, d, 64);
+    if (lane >= d) v += y;
   }
-  return buf[threadIdx.x];
+  return v;
 }
 
-__global__ __launch_bounds__(kThreads) void finalize_kernel(SampleArgs a) {
-  __shared__ Round rd;
-  __shared__ double scan[kThreads];
-  __shared__ int s_chunk, s_first, s_last, s_pos_last;
-  const int b = blockIdx.x;
+// One wave per sequence draws the round's last token by inverse CDF over the
+// residual (or bonus) weights: lanes own contiguous chunk ranges, then
+// contiguous 64-token runs of the chosen chunk; running sums are ordered wave
+// scans, so the draw is deterministic.
+constexpr int kFinalizeLanes = 64;
+constexpr int kTokPerLane = kChunk / kFinalizeLanes;
+
+__global__ __launch_bounds__(kFinalizeLanes) void finalize_kernel(SampleArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
   const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-  {  // the decision the residual pass made for this sequence
-    const int R = 2 * a.gamma + 1;
-    if (threadIdx.x < (unsigned)R) {
-      rd.M[threadIdx.x] = L.rmax[(size_t)b * R + threadIdx.x];
-      rd.iZ[threadIdx.x] = L.iz[(size_t)b * R + threadIdx.x];
-    }
-    if (threadIdx.x == 0) rd.n = L.nacc[b];
-    __syncthreads();
-  }
-  const float c_log2 = 1.4426950408889634f / a.temperature;
-  const int n = rd.n;
+  const int R = 2 * a.gamma + 1;
+  const int n = L.nacc[b];
+  const int tr = a.gamma + n, dr = n < a.gamma ? n : tr;
+  const float Mt = L.rmax[(size_t)b * R + tr], Md = L.rmax[(size_t)b * R + dr];
+  const double iZt = L.iz[(size_t)b * R + tr], iZd = L.iz[(size_t)b * R + dr];
+  const bool bonus = n == a.gamma;
   const double u = philox_uniform(a.seed, a.offset, b, n, 1);
 
-  // Chunk level: residual mass per chunk (or p's, if the residual has none).
-  double total = 0.0;
-  {
-    double v = 0.0;
-    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads) v += L.wsum[(size_t)b * a.n_chunks + c];
-    total = block_inclusive_scan(v, scan);
-    total = scan[kThreads - 1];
-    __syncthreads();
+  // Chunk level.
+  const int per = (a.n_chunks + 63) / 64;
+  const int c0 = min(a.n_chunks, lane * per), c1 = min(a.n_chunks, c0 + per);
+  double own_w = 0.0, own_p = 0.0;
+  int last_pos = -1;
+  for (int c = c0; c < c1; ++c) {
+    const double w = L.wsum[(size_t)b * a.n_chunks + c];
+    own_w += w;
+    own_p += L.psum[(size_t)b * a.n_chunks + c];
+    if (w > 0.0) last_pos = c;
   }
-  const bool use_p = !(total > 0.0);
-  const double* cs = (use_p ? L.psum : L.wsum) + (size_t)b * a.n_chunks;
+  double incl = wave_inclusive_scan(own_w);
+  double total = __shfl(incl, 63, 64);
+  const bool use_p = !(total > 0.0);  // residual without mass (rounding only): draw from p
   if (use_p) {
-    double v = 0.0;
-    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads) v += cs[c];
-    block_inclusive_scan(v, scan);
-    total = scan[kThreads - 1];
-    __syncthreads();
+    incl = wave_inclusive_scan(own_p);
+    total = __shfl(incl, 63, 64);
   }
   const double target = u * total;
-  // Thread t owns chunks [t*per, (t+1)*per): the first chunk whose running
-  // sum passes the target holds the draw.
-  const int per = (a.n_chunks + kThreads - 1) / kThreads;
-  const int c0 = min(a.n_chunks, (int)threadIdx.x * per), c1 = min(a.n_chunks, c0 + per);
-  double own = 0.0;
-  for (int c = c0; c < c1; ++c) own += cs[c];
-  const double incl = block_inclusive_scan(own, scan);
-  if (threadIdx.x == 0) {
-    s_chunk = 0x7fffffff;
-    s_pos_last = -1;
-    s_first = 0x7fffffff;
-    s_last = -1;
-  }
-  __syncthreads();
-  double run = incl - own;
-  for (int c = c0; c < c1; ++c) {
-    if (cs[c] > 0.0) atomicMax(&s_pos_last, c);
-    if (run + cs[c] > target) {
-      atomicMin(&s_chunk, c);
-      break;
-    }
-    run += cs[c];
-  }
-  __syncthreads();
-  const bool fallback = s_chunk == 0x7fffffff;
-  const int chunk = fallback ? max(s_pos_last, 0) : s_chunk;
-  // base = mass of the chunks before `chunk`
+  int chunk = 0x7fffffff;
   double before = 0.0;
-  for (int c = c0; c < c1; ++c)
-    if (c < chunk) before += cs[c];
-  block_inclusive_scan(before, scan);
-  const double base = scan[kThreads - 1];
-  __syncthreads();
+  {
+    double run = incl - (use_p ? own_p : own_w);
+    for (int c = c0; c < c1; ++c) {
+      const double w = use_p ? L.psum[(size_t)b * a.n_chunks + c] : L.wsum[(size_t)b * a.n_chunks + c];
+      if (use_p && w > 0.0) last_pos = c;
+      if (run + w > target) {
+        chunk = c;
+        before = run;
+        break;
+      }
+      run += w;
+    }
+  }
+  // The first crossing chunk over the wave (or, if rounding left none, the
+  // last chunk with mass).
+  int best = chunk;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) best = min(best, __shfl_xor(best, x, 64));
+  const bool fallback = best == 0x7fffffff;
+  if (fallback) {
+    int lp = last_pos;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) lp = max(lp, __shfl_xor(lp, x, 64));
+    best = max(lp, 0);
+  }
+  const unsigned long long owner = __ballot(chunk == best);
+  const double base = fallback ? 0.0 : __shfl(before, owner ? __ffsll(owner) - 1 : 0, 64);
 
-  // Token level inside the chunk: thread t owns tokens [lo + 16t, lo + 16t + 16).
-  const int lo = chunk * kChunk, hi = min(a.V, lo + kChunk);
-  const int t0 = min(hi, lo + kPerThread * (int)threadIdx.x), t1 = min(hi, t0 + kPerThread);
-  double w[kPerThread];
+  // Token level inside the chosen chunk.
+  const int lo = best * kChunk, hi = min(a.V, lo + kChunk);
+  const int t0 = min(hi, lo + kTokPerLane * lane), t1 = min(hi, t0 + kTokPerLane);
+  const float c_log2 = 1.4426950408889634f / a.temperature;
+  const float* trow = row_ptr(a, b, tr);
+  const float* drow = row_ptr(a, b, dr);
+  float xt[kTokPerLane], xd[kTokPerLane];
+#pragma unroll
+  for (int k = 0; k < kTokPerLane; ++k) {
+    const int t = t0 + k;
+    xt[k] = t < t1 ? trow[t] : -__builtin_huge_valf();
+    xd[k] = t < t1 ? drow[t] : -__builtin_huge_valf();
+  }
+  double w[kTokPerLane];
   double local = 0.0;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    w[k] = 0.0;
-    if (t0 + k < t1) {
-      double p;
-      const double r = draw_weight(a, rd, b, t0 + k, c_log2, &p);
-      w[k] = use_p ? p : r;
-      local += w[k];
-    }
+  for (int k = 0; k < kTokPerLane; ++k) {
+    const double p = (double)scaled_exp(xt[k], Mt, c_log2) * iZt;
+    const double q = bonus ? 0.0 : (double)scaled_exp(xd[k], Md, c_log2) * iZd;
+    w[k] = use_p ? p : (p > q ? p - q : 0.0);
+    local += w[k];
   }
-  const double tincl = block_inclusive_scan(local, scan);
-  double trun = base + tincl - local;
+  const double tincl = wave_inclusive_scan(local);
+  double run = base + tincl - local;
   int first = 0x7fffffff, last = -1;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    if (t0 + k < t1) {
-      if (w[k] > 0.0) last = t0 + k;
-      trun += w[k];
-      if (first == 0x7fffffff && !fallback && trun > target) first = t0 + k;
-    }
+  for (int k = 0; k < kTokPerLane; ++k) {
+    if (w[k] > 0.0) last = t0 + k;
+    run += w[k];
+    if (first == 0x7fffffff && !fallback && run > target) first = t0 + k;
   }
-  if (first != 0x7fffffff) atomicMin(&s_first, first);
-  if (last >= 0) atomicMax(&s_last, last);
-  __syncthreads();
-  if (threadIdx.x <= (unsigned)a.gamma) {
-    const int i = threadIdx.x;
-    const int token = s_first != 0x7fffffff ? s_first : s_last;
-    a.out_tokens[(size_t)b * (a.gamma + 1) + i] =
-        i < n ? a.draft_tokens[(size_t)b * a.gamma + i] : (i == n ? token : -1);
-    if (i == 0) a.num_accepted[b] = n;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) {
+    first = min(first, __shfl_xor(first, x, 64));
+    last = max(last, __shfl_xor(last, x, 64));
+  }
+  if (lane <= a.gamma) {
+    const int token = first != 0x7fffffff ? first : last;
+    a.out_tokens[(size_t)b * (a.gamma + 1) + lane] =
+        lane < n ? a.draft_tokens[(size_t)b * a.gamma + lane] : (lane == n ? token : -1);
+    if (lane == 0) a.num_accepted[b] = n;
   }
 }
 
@@ -435,10 +437,13 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(stats_kernel, dim3(a.n_chunks, R, a.B), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decide_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(residual_kernel, dim3(a.n_chunks, a.B), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(kFinalizeLanes), 0, stream, a);
   return hipGetLastError();
 }
 

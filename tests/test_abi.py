@@ -84,9 +84,12 @@ def test_invalid_call_arguments():
     assert lib.s3r_dense_verify_attn(kv, v, 0, 0.1, 0, v, v, big, None) == 1
     assert lib.s3r_dense_verify_attn(kv, None, 5, 0.1, 0, v, v, big, None) == 1
     assert lib.s3r_dense_verify_attn(kv, v, 33, 0.1, 0, v, v, big, None) == 2     # 2*33 rows > 64
-    wneed = lib.s3r_attn_workspace(kv, 5, 8)
+    kv32 = ctypes.byref(_kv(kv_dtype=_lib.S3R_F32))  # fp32 KV always merges through the workspace
+    wneed = lib.s3r_attn_workspace(kv32, 5, 8)
     assert wneed > 0
-    assert lib.s3r_dense_verify_attn(kv, v, 5, 0.1, 0, v, v, wneed - 1, None) == 3
+    assert lib.s3r_dense_verify_attn(kv32, v, 5, 0.1, 0, v, v, wneed - 1, None) == 3
+    # bf16 KV whose splits fit one workgroup merges in LDS and needs no workspace
+    assert lib.s3r_attn_workspace(kv, 5, 8) == 0
     s = lib.s3r_spec_sample
     assert s(0, 4, 1024, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
     assert s(2, 0, 1024, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 1
