@@ -2,8 +2,8 @@
 
 A step is one round of "S3R: Fast and Faithful RL Rollouts via
 Self-Sparse Speculative Decoding" (Abstract) for one attention layer:
-  for j in 0..gamma-1: page_bounds_update (tail page) -> page_select ->
-                       sparse_draft_attn (query position L-1+j)
+  for j in 0..gamma-1: sparse_draft_step = tail-page bounds refresh ->
+                       page select -> sparse draft attention (query L-1+j)
   dense_verify_attn (gamma+1 causal queries over the complete KV)
   spec_sample (accept/reject, residual or bonus draw)
 over the Qwen3-8B-shaped layer: bf16 paged KV, 32 q / 8 kv heads, head dim 128,
@@ -103,6 +103,8 @@ def main():
     v_out = torch.empty((B, gamma + 1, Hq, D), dtype=torch.bfloat16, device=dev)
     ws_sel = torch.empty(max(1, s3r.page_select_workspace(kv, budget)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, s3r.attn_workspace(kv, 1, k)), dtype=torch.uint8, device=dev)
+    ws_step = torch.empty(max(1, s3r.sparse_draft_step_workspace(kv, budget)), dtype=torch.uint8,
+                          device=dev)
     ws_v = torch.empty(max(1, s3r.attn_workspace(kv, gamma + 1, wl.max_pages)), dtype=torch.uint8,
                        device=dev)
     ws_s = torch.empty(max(1, s3r.spec_sample_workspace(B, gamma, V)), dtype=torch.uint8, device=dev)
@@ -111,9 +113,8 @@ def main():
 
     def draft_step(j):
         kv.set_seq_lens(wl.seq_lens[j])
-        s3r.page_bounds_update(kv, bounds, first_pos=first_pos[j], max_pages_touched=1)
-        s3r.page_select(kv, bounds, q_draft[j], budget, scale, sel, nsel, workspace=ws_sel)
-        s3r.sparse_draft_attn(kv, q_draft[j], sel, scale, out=d_out[j], workspace=ws_d)
+        s3r.sparse_draft_step(kv, bounds, q_draft[j], budget, scale, refresh_from=first_pos[j],
+                              selected=sel, num_selected=nsel, out=d_out[j], workspace=ws_step)
 
     def verify():
         kv.set_seq_lens(wl.seq_lens[gamma])
@@ -184,6 +185,10 @@ def main():
                                                       workspace=ws_d), reps)
     t_bounds = time_call(lambda: s3r.page_bounds_update(kv, bounds, first_pos=first_pos[0],
                                                         max_pages_touched=1), reps)
+    t_step = time_call(lambda: s3r.sparse_draft_step(kv, bounds, q_draft[0], budget, scale,
+                                                     refresh_from=first_pos[0], selected=sel,
+                                                     num_selected=nsel, out=d_out[0],
+                                                     workspace=ws_step), reps)
     kv.set_seq_lens(wl.seq_lens[gamma])
     t_verify = time_call(lambda: s3r.dense_verify_attn(kv, wl.q_verify, scale, out=v_out,
                                                        workspace=ws_v), reps)
@@ -224,7 +229,7 @@ def main():
         "verify_kv_gbs": round(verify_gbs, 1),
         "step_bytes": {k2: int(v2) for k2, v2 in parts.items()},
         "launch_us": {"page_bounds_update": round(t_bounds, 2), "page_select": round(t_select, 2),
-                      "sparse_draft_attn": round(t_draft, 2),
+                      "sparse_draft_attn": round(t_draft, 2), "sparse_draft_step": round(t_step, 2),
                       "dense_verify_attn": round(t_verify, 2), "spec_sample": round(t_sample, 2)},
         "roofline": {"kernel": "dense_verify_attn (attn_bf16_kernel + split combine)",
                      "bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,

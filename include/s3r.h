@@ -139,6 +139,29 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const in
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * s3r_sparse_draft_step: one whole draft step in two kernel launches, the
+ * fused form of
+ *   s3r_page_bounds_update(refresh_from)  (when refresh_from is not NULL)
+ *   s3r_page_select(q, budget_tokens)     -> selected, num_selected
+ *   s3r_sparse_draft_attn(q, selected)    -> out
+ * with identical results. The score pass refreshes the bounds of pages from
+ * refresh_from[b] / P to the tail (writing them to `bounds`) as it scores them;
+ * each attention workgroup then selects its (sequence, kv head)'s pages by the
+ * same exact top-k, in LDS, and attends over them. fp32 KV (and selections too
+ * large for LDS) run the three calls' kernels instead.
+ *   bounds        in/out, [num_phys_pages][Hkv][2][D] kv dtype.
+ *   refresh_from  [B] int32 or NULL.
+ *   selected, num_selected: out, as s3r_page_select.   out: as s3r_sparse_draft_attn.
+ * Errors: as the three calls; WORKSPACE_TOO_SMALL if workspace_bytes <
+ * s3r_sparse_draft_step_workspace().
+ */
+size_t s3r_sparse_draft_step_workspace(const s3r_paged_kv* kv, int32_t budget_tokens);
+s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
+                                 const void* q, int32_t budget_tokens, float softmax_scale,
+                                 int32_t* selected, int32_t* num_selected, s3r_dtype out_dtype,
+                                 void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * s3r_dense_verify_attn: full-attention verification of the draft ("dense
  * verification still requires the complete historical KV cache", S3R
  * Abstract). Query i = 0..n_q-1 of sequence b sits at position

@@ -35,17 +35,35 @@ s3r_status check_workspace(void* ws, size_t have, size_t need) {
 
 s3r_status from_hip(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
 
-s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* sel, int32_t ksel,
-                         int32_t n_q, float scale, s3r_dtype out_dtype, void* out, void* ws,
-                         size_t ws_bytes, void* stream) {
+s3r::AttnArgs attn_args(const s3r_paged_kv* kv, const s3r::SplitPlan& plan, const void* q,
+                        const int32_t* sel, int32_t ksel, int32_t n_q, float scale,
+                        s3r_dtype out_dtype, void* out, void* ws);
+
+s3r_status check_attention(const s3r_paged_kv* kv, const void* q, int32_t n_q, float scale,
+                           s3r_dtype out_dtype, void* out) {
   if (s3r_status s = check_kv(kv)) return s;
   if (q == nullptr || out == nullptr || n_q < 1 || !isfinite(scale)) return S3R_ERR_INVALID_ARGUMENT;
   if (out_dtype != S3R_F32 && out_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
   const int32_t G = kv->num_q_heads / kv->num_kv_heads;
   if ((int64_t)G * n_q > kMaxRows) return S3R_ERR_UNSUPPORTED;
+  return S3R_OK;
+}
+
+s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* sel, int32_t ksel,
+                         int32_t n_q, float scale, s3r_dtype out_dtype, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (s3r_status s = check_attention(kv, q, n_q, scale, out_dtype, out)) return s;
   const int32_t max_items = sel ? ksel : kv->max_pages_per_seq;
   const s3r::SplitPlan plan = s3r::plan_attention(*kv, n_q, max_items);
   if (s3r_status s = check_workspace(ws, ws_bytes, plan.workspace_bytes)) return s;
+  const s3r::AttnArgs a = attn_args(kv, plan, q, sel, ksel, n_q, scale, out_dtype, out, ws);
+  return from_hip(s3r::launch_attention(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+s3r::AttnArgs attn_args(const s3r_paged_kv* kv, const s3r::SplitPlan& plan, const void* q,
+                        const int32_t* sel, int32_t ksel, int32_t n_q, float scale,
+                        s3r_dtype out_dtype, void* out, void* ws) {
+  const int32_t G = kv->num_q_heads / kv->num_kv_heads;
   s3r::AttnArgs a{};
   a.k_pool = kv->k_pool;
   a.v_pool = kv->v_pool;
@@ -73,7 +91,55 @@ s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* s
   a.lds_region_bytes = plan.lds_region_bytes;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_bf16 = out_dtype == S3R_BF16;
-  return from_hip(s3r::launch_attention(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
+  return a;
+}
+
+s3r::SelectArgs select_args(const s3r_paged_kv* kv, const void* bounds, const void* q,
+                            int32_t budget_tokens, float scale, int32_t* selected,
+                            int32_t* num_selected, void* scores) {
+  s3r::SelectArgs a{};
+  a.bounds = bounds;
+  a.k_pool = kv->k_pool;
+  a.q = q;
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.scores = static_cast<float*>(scores);
+  a.selected = selected;
+  a.num_selected = num_selected;
+  a.B = kv->num_seqs;
+  a.Hq = kv->num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = kv->num_q_heads / kv->num_kv_heads;
+  a.D = kv->head_dim;
+  a.max_pages = kv->max_pages_per_seq;
+  a.k = budget_tokens / kv->page_size;
+  a.scale = scale;
+  return a;
+}
+
+// The fused draft step keeps the page keys, then the selection list, in LDS
+// beside the per-wave regions; it needs bf16 KV and at most 64 KB.
+struct DraftStepPlan {
+  s3r::SplitPlan attn;
+  size_t select_ws;
+  bool fused;
+  int32_t list_offset;
+  size_t workspace_bytes;
+};
+
+DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
+  DraftStepPlan p{};
+  const int32_t k = budget_tokens / kv.page_size;
+  p.attn = s3r::plan_attention(kv, 1, k);
+  p.select_ws = s3r::select_workspace_bytes(kv.num_seqs, kv.num_kv_heads, kv.max_pages_per_seq);
+  const size_t regions = (size_t)p.attn.lds_region_bytes * p.attn.waves_per_group;
+  const size_t keys = sizeof(uint32_t) * (size_t)kv.max_pages_per_seq;
+  const size_t list_offset = ((regions > keys ? regions : keys) + 15) & ~(size_t)15;
+  p.list_offset = (int32_t)list_offset;
+  p.fused = kv.kv_dtype == S3R_BF16 && list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
+  p.workspace_bytes = p.fused ? p.select_ws + p.attn.workspace_bytes
+                              : (p.select_ws > p.attn.workspace_bytes ? p.select_ws : p.attn.workspace_bytes);
+  return p;
 }
 
 }  // namespace
@@ -128,22 +194,8 @@ s3r_status s3r_page_select(const s3r_paged_kv* kv, const void* bounds, const voi
   if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::select_workspace_bytes(kv->num_seqs, kv->num_kv_heads, kv->max_pages_per_seq);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
-  s3r::SelectArgs a{};
-  a.bounds = bounds;
-  a.q = q;
-  a.page_table = kv->page_table;
-  a.seq_lens = kv->seq_lens;
-  a.scores = static_cast<float*>(workspace);
-  a.selected = selected;
-  a.num_selected = num_selected;
-  a.B = kv->num_seqs;
-  a.Hq = kv->num_q_heads;
-  a.Hkv = kv->num_kv_heads;
-  a.G = kv->num_q_heads / kv->num_kv_heads;
-  a.D = kv->head_dim;
-  a.max_pages = kv->max_pages_per_seq;
-  a.k = budget_tokens / kv->page_size;
-  a.scale = softmax_scale;
+  const s3r::SelectArgs a = select_args(kv, bounds, q, budget_tokens, softmax_scale, selected,
+                                        num_selected, workspace);
   return from_hip(s3r::launch_select(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -153,6 +205,60 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const in
   if (selected == nullptr || k < 1) return S3R_ERR_INVALID_ARGUMENT;
   return run_attention(kv, q, selected, k, 1, softmax_scale, out_dtype, out, workspace,
                        workspace_bytes, stream);
+}
+
+size_t s3r_sparse_draft_step_workspace(const s3r_paged_kv* kv, int32_t budget_tokens) {
+  if (check_kv(kv) != S3R_OK || budget_tokens < kv->page_size) return 0;
+  return plan_draft_step(*kv, budget_tokens).workspace_bytes;
+}
+
+s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
+                                 const void* q, int32_t budget_tokens, float softmax_scale,
+                                 int32_t* selected, int32_t* num_selected, s3r_dtype out_dtype,
+                                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (s3r_status s = check_attention(kv, q, 1, softmax_scale, out_dtype, out)) return s;
+  if (bounds == nullptr || selected == nullptr || num_selected == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (budget_tokens < kv->page_size) return S3R_ERR_INVALID_ARGUMENT;
+  if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
+  const DraftStepPlan plan = plan_draft_step(*kv, budget_tokens);
+  if (s3r_status s = check_workspace(workspace, workspace_bytes, plan.workspace_bytes)) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t k = budget_tokens / kv->page_size;
+  s3r::SelectArgs sa = select_args(kv, bounds, q, budget_tokens, softmax_scale, selected,
+                                   num_selected, workspace);
+  if (plan.fused) {
+    sa.refresh_from = refresh_from;
+    sa.bounds_out = bounds;
+    if (hipError_t e = s3r::launch_scores(sa, kv->kv_dtype, st)) return from_hip(e);
+    char* partials = static_cast<char*>(workspace) + plan.select_ws;
+    s3r::AttnArgs a = attn_args(kv, plan.attn, q, nullptr, k, 1, softmax_scale, out_dtype, out,
+                                plan.attn.workspace_bytes ? partials : nullptr);
+    a.scores = static_cast<const float*>(workspace);
+    a.sel_out = selected;
+    a.nsel_out = num_selected;
+    a.list_offset = plan.list_offset;
+    return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
+  }
+  // Unfused: bounds refresh, then select, then attention (stream order makes
+  // the workspace reusable between them).
+  if (refresh_from) {
+    s3r::BoundsArgs ba{};
+    ba.k_pool = kv->k_pool;
+    ba.page_table = kv->page_table;
+    ba.seq_lens = kv->seq_lens;
+    ba.first_pos = refresh_from;
+    ba.bounds = bounds;
+    ba.B = kv->num_seqs;
+    ba.Hkv = kv->num_kv_heads;
+    ba.D = kv->head_dim;
+    ba.max_pages = kv->max_pages_per_seq;
+    ba.pages_y = kv->max_pages_per_seq;
+    if (hipError_t e = s3r::launch_bounds(ba, kv->kv_dtype, st)) return from_hip(e);
+  }
+  if (hipError_t e = s3r::launch_select(sa, kv->kv_dtype, st)) return from_hip(e);
+  const s3r::AttnArgs a = attn_args(kv, plan.attn, q, selected, k, 1, softmax_scale, out_dtype, out,
+                                    plan.attn.workspace_bytes ? workspace : nullptr);
+  return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
 }
 
 s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t n_q,

@@ -23,6 +23,7 @@
 // per window.
 #include "s3r_common.h"
 #include "s3r_internal.h"
+#include "s3r_topk.h"
 
 namespace s3r {
 namespace {
@@ -236,7 +237,12 @@ constexpr int bf16_waves_per_simd() { return kNB == 1 ? 2 : 1; }
 // has drained) its (m, l, o) partial; after a barrier the workgroup merges the
 // kW partials and writes either the final output (one group per (sequence,
 // head)) or one group partial for the global combine.
-template <int kD, int kNB, bool kSparse, int kW>
+//
+// kSelect (the fused draft step): the workgroup first selects its (sequence,
+// kv head)'s pages itself, by an exact block top-k over the page scores in
+// LDS, and attends over that list; group 0 also writes the list and the count
+// out, as s3r_page_select would.
+template <int kD, int kNB, bool kSparse, int kW, bool kSelect = false>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(bf16_waves_per_simd<kNB>(), 8)))
 void attn_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
@@ -248,13 +254,33 @@ void attn_bf16_kernel(AttnArgs a) {
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
   const int g0 = group * kW * a.pages_per_split;
-  if (g0 >= n_items && a.n_groups > 1) return;  // the global combine skips this group
+  // the global combine skips an empty group (group 0 still publishes the selection)
+  if (g0 >= n_items && a.n_groups > 1 && !(kSelect && group == 0)) return;
   const int j0 = g0 + wave * a.pages_per_split;
   const int j1 = min(j0 + a.pages_per_split, n_items);
   const bool active = j0 < n_items;
 
   extern __shared__ int4 lds[];
   char* region = reinterpret_cast<char*>(lds) + (size_t)wave * a.lds_region_bytes;
+  const int32_t* sel_row = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
+  if constexpr (kSelect) {
+    __shared__ TopkShared<64 * kW> sh;
+    int32_t* list = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(lds) + a.list_offset);
+    const int k = a.ksel;
+    if (k < n_pages)
+      block_topk<64 * kW>(a.scores + (size_t)bh * a.max_pages, n_pages, k,
+                          reinterpret_cast<uint32_t*>(lds), sh, list);
+    else
+      for (int t = threadIdx.x; t < k; t += 64 * kW) list[t] = t < n_pages ? t : -1;
+    __syncthreads();
+    if (group == 0) {
+      int32_t* out = a.sel_out + (size_t)bh * k;
+      for (int t = threadIdx.x; t < k; t += 64 * kW) out[t] = list[t];
+      if (h == 0 && threadIdx.x == 0) a.nsel_out[b] = min(k, n_pages);
+    }
+    if (g0 >= n_items && a.n_groups > 1) return;  // uniform: the whole group
+    sel_row = list;
+  }
   float m_run[kNB], l_run[kNB];
   f32x4 acc[kNB][kD / 16];
 #pragma unroll
@@ -269,7 +295,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-    const int32_t* sel = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
+    const int32_t* sel = sel_row;
     const uint16_t* qg = static_cast<const uint16_t*>(a.q);
 
     bf16x8 qb[kNB][kD / 32];
@@ -567,6 +593,24 @@ hipError_t launch_typed(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int kD>
+hipError_t launch_fused_draft(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_groups));
+  const size_t lds = (size_t)a.list_offset + sizeof(int32_t) * a.ksel;
+  switch (a.waves_per_group) {
+    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 1, true>), grid, dim3(64), lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 2, true>), grid, dim3(128), lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 4, true>), grid, dim3(256), lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, true>), grid, dim3(512), lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_groups == 1) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<kD, true>), dim3((unsigned)((size_t)a.B * a.nq * a.Hq)),
+                     dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int kD, bool kSparse>
 hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
   switch ((a.rows + 15) / 16) {
@@ -626,6 +670,10 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
 }
 
 hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream) {
+  if (a.scores != nullptr) {  // fused draft step: bf16, one row block
+    if (kv_dtype != S3R_BF16 || a.rows > 16) return hipErrorInvalidValue;
+    return a.D == 128 ? launch_fused_draft<128>(a, stream) : launch_fused_draft<64>(a, stream);
+  }
   const bool sparse = a.sel != nullptr;
   if (a.D == 128)
     return sparse ? launch_nb<128, true>(a, kv_dtype, stream) : launch_nb<128, false>(a, kv_dtype, stream);

@@ -41,6 +41,12 @@ struct AttnArgs {
   int32_t waves_per_group, n_groups, lds_region_bytes;
   float scale_log2;       // softmax_scale * log2(e)
   int32_t out_bf16;
+  // Fused draft step only: page scores [B][Hkv][max_pages]; the selection is
+  // built in LDS at list_offset and published to sel_out / nsel_out.
+  const float* scores;
+  int32_t* sel_out;
+  int32_t* nsel_out;
+  int32_t list_offset;
 };
 
 hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
@@ -58,6 +64,9 @@ hipError_t launch_bounds(const BoundsArgs& a, s3r_dtype kv_dtype, hipStream_t st
 
 struct SelectArgs {
   const void* bounds;
+  void* bounds_out;             // == bounds when refresh_from is set (bf16 only)
+  const void* k_pool;
+  const int32_t* refresh_from;  // [B] or nullptr: pages from refresh_from/P on are recomputed
   const void* q;
   const int32_t* page_table;
   const int32_t* seq_lens;
@@ -69,6 +78,9 @@ struct SelectArgs {
 };
 
 hipError_t launch_select(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
+// Scores only (no top-k), with the optional bounds refresh: the first half of
+// the fused draft step.
+hipError_t launch_scores(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
 size_t select_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_pages);
 int32_t select_max_pages_supported();
 

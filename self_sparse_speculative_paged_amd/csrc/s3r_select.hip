@@ -14,6 +14,7 @@
 // vectors: for bf16 bounds, v_dot2_f32_bf16 on the packed bounds as loaded.
 #include "s3r_common.h"
 #include "s3r_internal.h"
+#include "s3r_topk.h"
 
 namespace s3r {
 namespace {
@@ -107,21 +108,78 @@ __global__ __launch_bounds__(64) void bounds_kernel(BoundsArgs a) {
   }
 }
 
+// Recomputes the bf16 bounds of page j of (sequence b, kv head h) from K over
+// its valid tokens, writes them to the bounds buffer and returns them packed as
+// loaded: lane c of the page group owns d = 8c .. 8c+7.
+template <int kD>
+__device__ __forceinline__ void refresh_page_bounds(const SelectArgs& a, int b, int h, int j,
+                                                    int seq_len, int phys, int c, uint4& kmin,
+                                                    uint4& kmax) {
+  const int valid = min(kPage, seq_len - kPage * j);
+  const uint16_t* kb =
+      static_cast<const uint16_t*>(a.k_pool) + ((size_t)phys * a.Hkv + h) * kPage * kD + 8 * c;
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = __builtin_huge_valf();
+    mx[e] = -__builtin_huge_valf();
+  }
+  // Two halves of 8 rows: each half's loads are in flight together.
+#pragma unroll
+  for (int t0 = 0; t0 < kPage; t0 += kPage / 2) {
+    uint4 rows[kPage / 2];
+#pragma unroll
+    for (int t = 0; t < kPage / 2; ++t)
+      rows[t] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + t < valid ? t0 + t : 0) * kD);
+#pragma unroll
+    for (int t = 0; t < kPage / 2; ++t) {
+      if (t0 + t < valid) {
+        const uint32_t w[4] = {rows[t].x, rows[t].y, rows[t].z, rows[t].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+          mn[2 * e] = fminf(mn[2 * e], lo);
+          mx[2 * e] = fmaxf(mx[2 * e], lo);
+          mn[2 * e + 1] = fminf(mn[2 * e + 1], hi);
+          mx[2 * e + 1] = fmaxf(mx[2 * e + 1], hi);
+        }
+      }
+    }
+  }
+  uint32_t pmn[4], pmx[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pmn[e] = (uint32_t)f32_to_bf16_bits(mn[2 * e]) | ((uint32_t)f32_to_bf16_bits(mn[2 * e + 1]) << 16);
+    pmx[e] = (uint32_t)f32_to_bf16_bits(mx[2 * e]) | ((uint32_t)f32_to_bf16_bits(mx[2 * e + 1]) << 16);
+  }
+  kmin = make_uint4(pmn[0], pmn[1], pmn[2], pmn[3]);
+  kmax = make_uint4(pmx[0], pmx[1], pmx[2], pmx[3]);
+  uint16_t* pb = static_cast<uint16_t*>(a.bounds_out) + ((size_t)phys * a.Hkv + h) * 2 * kD + 8 * c;
+  *reinterpret_cast<uint4*>(pb) = kmin;
+  *reinterpret_cast<uint4*>(pb + kD) = kmax;
+}
+
 // ---------------------------------------------------------------------------
 // Scores: a group of D/8 lanes scores one page for every q head of the kv
 // head; a wave scores 64/(D/8) pages per step.
 // ---------------------------------------------------------------------------
 template <typename T, int kD, int kG>
-__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kG <= 4 ? 4 : 2, 8)))
+void score_kernel(SelectArgs a) {
   constexpr int kLpp = kD / 8;            // lanes per page (8 d per lane)
   constexpr int kGroups = 256 / kLpp;     // page groups per block
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int seq_len = a.seq_lens[b];
   const int n = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
-  if (a.k >= n) return;  // every page is taken; the top-k pass writes 0..n-1
   const int c = threadIdx.x % kLpp, grp = threadIdx.x / kLpp;
   const int start = blockIdx.y * kSelectPagesPerBlock;
+  // Pages from `rf` on get their bounds recomputed from K first (bf16 only).
+  int rf = 0x7fffffff;
+  if constexpr (sizeof(T) == 2)
+    if (a.refresh_from) rf = max(a.refresh_from[b], 0) / kPage;
+  const bool score = a.k < n;  // otherwise every page is taken: the top-k pass writes 0..n-1
+  if (!score && (rf >= n || start + kSelectPagesPerBlock <= rf)) return;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
   float* scores = a.scores + (size_t)bh * a.max_pages;
   constexpr int kIter = kSelectPagesPerBlock / kGroups;
@@ -148,20 +206,9 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
         qn[g][e / 2][e % 2] = neg ? v : z;
       }
     const uint16_t* bb = static_cast<const uint16_t*>(a.bounds);
-    uint4 kmin[kIter], kmax[kIter];
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const uint16_t* pb = bb + ((size_t)(phys[i] < 0 ? 0 : phys[i]) * a.Hkv + h) * 2 * kD + 8 * c;
-      if (phys[i] >= 0) {
-        kmin[i] = load_nt16<uint4>(pb);
-        kmax[i] = load_nt16<uint4>(pb + kD);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      if (phys[i] < 0) continue;  // uniform within the page group
-      const uint32_t mn[4] = {kmin[i].x, kmin[i].y, kmin[i].z, kmin[i].w};
-      const uint32_t mx[4] = {kmax[i].x, kmax[i].y, kmax[i].z, kmax[i].w};
+    auto score_of = [&](const uint4& lo, const uint4& hi) {
+      const uint32_t mn[4] = {lo.x, lo.y, lo.z, lo.w};
+      const uint32_t mx[4] = {hi.x, hi.y, hi.z, hi.w};
       float best = -__builtin_huge_valf();
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -173,7 +220,42 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
         }
         best = fmaxf(best, group_sum<kLpp>(acc));
       }
-      if (c == 0) scores[start + grp + kGroups * i] = best * a.scale;
+      return best * a.scale;
+    };
+    // Pages before the refresh point: all bounds loads in flight together.
+    uint4 kmin[kIter], kmax[kIter];
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int j = start + grp + kGroups * i;
+      if (phys[i] >= 0 && j < rf) {
+        const uint16_t* pb = bb + ((size_t)phys[i] * a.Hkv + h) * 2 * kD + 8 * c;
+        kmin[i] = load_nt16<uint4>(pb);
+        kmax[i] = load_nt16<uint4>(pb + kD);
+      }
+    }
+    if (score) {
+#pragma unroll
+      for (int i = 0; i < kIter; ++i) {
+        const int j = start + grp + kGroups * i;
+        if (phys[i] < 0 || j >= rf) continue;  // uniform within the page group
+        const float sc = score_of(kmin[i], kmax[i]);
+        if (c == 0) scores[j] = sc;
+      }
+    }
+    // Pages from the refresh point on (normally just the tail page): bounds
+    // recomputed from K, written back, then scored.
+    if (start + kSelectPagesPerBlock > rf) {
+#pragma unroll 1
+      for (int i = 0; i < kIter; ++i) {
+        const int j = start + grp + kGroups * i;
+        if (phys[i] < 0 || j < rf) continue;
+        uint4 lo, hi;
+        refresh_page_bounds<kD>(a, b, h, j, seq_len, phys[i], c, lo, hi);
+        if (score) {
+          const float sc = score_of(lo, hi);
+          if (c == 0) scores[j] = sc;
+        }
+      }
     }
   } else {
     float qp[kG][8], qn[kG][8];
@@ -213,49 +295,14 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
   }
 }
 
-// Exclusive prefix sum over the threads of a block (fixed order).
-template <int kThreadsPerBlock>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  __syncthreads();
-  return base + incl - v;
-}
-
-// Float -> uint32 with the same order (larger float, larger key). -0 is folded
-// into +0 first so equal scores always tie.
-__device__ __forceinline__ uint32_t order_key(float s) {
-  const uint32_t u = __float_as_uint(s + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// ---------------------------------------------------------------------------
-// Top-k: exact radix select of the k-th largest key, then a stable compaction
-// in page order, which emits the kept pages ascending. Ties on the threshold
-// key keep the lowest page indices. Key bits shared by every key (the common
-// prefix of the block's min and max key) are skipped; the rest are resolved
-// 9 bits per pass.
-// ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
-constexpr int kDigitBits = 9;
-constexpr int kBins = 1 << kDigitBits;
 
+// One block per (sequence, kv head): the k best pages of its scores, ascending,
+// -1 padded; every page when k >= n.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wave_tot[kTopkThreads / 64];
-  __shared__ uint32_t s_min[kTopkThreads / 64], s_max[kTopkThreads / 64];
-  __shared__ uint32_t s_digit, s_krem;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ TopkShared<kTopkThreads> sh;
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int seq_len = a.seq_lens[b];
@@ -267,110 +314,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
     for (int t = tid; t < k; t += kTopkThreads) out[t] = t < n ? t : -1;
     return;
   }
-  const float* sc = a.scores + (size_t)bh * a.max_pages;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  // Scores are loaded 8 per thread at a time, all in flight together.
-  for (int j0 = 0; j0 < n; j0 += 8 * kTopkThreads) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + tid + kTopkThreads * e;
-      v[e] = j < n ? sc[j] : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + tid + kTopkThreads * e;
-      if (j < n) {
-        const uint32_t key = order_key(v[e]);
-        keys[j] = key;
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-      }
-    }
-  }
-  for (int x = 32; x >= 1; x >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, x, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, x, 64));
-  }
-  if (lane == 0) {
-    s_min[wave] = kmin;
-    s_max[wave] = kmax;
-  }
-  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
-  __syncthreads();
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
-    kmin = min(kmin, s_min[w]);
-    kmax = max(kmax, s_max[w]);
-  }
-  const int varying = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));
-  uint32_t prefix = kmin & (varying >= 32 ? 0u : ~((1u << varying) - 1u));
-  uint32_t mask = varying >= 32 ? 0u : ~((1u << varying) - 1u);
-  uint32_t krem = (uint32_t)k;
-  for (int lo_bit = varying - kDigitBits; lo_bit > -kDigitBits; lo_bit -= kDigitBits) {
-    const int shift = max(lo_bit, 0);
-    const int width = lo_bit >= 0 ? kDigitBits : kDigitBits + lo_bit;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int j0 = 0; j0 < n; j0 += kTopkThreads) {
-      const int j = j0 + tid;
-      const uint32_t key = j < n ? keys[j] : 0u;
-      if (j < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // Lane l holds the 8 bins 8l..8l+7 counted from the top digit down.
-      constexpr int kPer = kBins / 64;
-      uint32_t cnt[kPer], own = 0;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        cnt[e] = hist[kBins - 1 - (kPer * lane + e)];
-        own += cnt[e];
-      }
-      uint32_t incl = own;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-      }
-      uint32_t above = incl - own;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        if (above < krem && above + cnt[e] >= krem) {
-          s_digit = (uint32_t)(kBins - 1 - (kPer * lane + e));
-          s_krem = krem - above;
-        }
-        above += cnt[e];
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= dmask << shift;
-    krem = s_krem;
-    for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-  }
-  const uint32_t thr = prefix;
-
-  // Contiguous chunk per thread, scanned twice: equal-key ranks, then output slots.
-  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
-  const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
-  uint32_t n_eq = 0;
-  for (int j = lo; j < hi; ++j) n_eq += keys[j] == thr;
-  const uint32_t eq_before = block_exclusive_scan<kTopkThreads>(n_eq, wave_tot);
-  uint32_t n_take = 0, eq_rank = eq_before;
-  for (int j = lo; j < hi; ++j) {
-    const uint32_t key = keys[j];
-    if (key > thr) ++n_take;
-    else if (key == thr) n_take += (eq_rank++ < krem);
-  }
-  const uint32_t slot0 = block_exclusive_scan<kTopkThreads>(n_take, wave_tot);
-  uint32_t slot = slot0;
-  eq_rank = eq_before;
-  for (int j = lo; j < hi; ++j) {
-    const uint32_t key = keys[j];
-    bool take = key > thr;
-    if (key == thr) take = (eq_rank++ < krem);
-    if (take && slot < (uint32_t)k) out[slot++] = j;
-  }
+  block_topk<kTopkThreads>(a.scores + (size_t)bh * a.max_pages, n, k, keys, sh, out);
 }
 
 template <typename T, int kD>
@@ -409,14 +353,16 @@ hipError_t launch_bounds(const BoundsArgs& a, s3r_dtype dt, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) {
+hipError_t launch_scores(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) {
   const int ychunks = max(1, (a.max_pages + kSelectPagesPerBlock - 1) / kSelectPagesPerBlock);
   const dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)ychunks);
-  hipError_t e;
   if (dt == S3R_BF16)
-    e = a.D == 128 ? launch_score<uint16_t, 128>(a, grid, stream) : launch_score<uint16_t, 64>(a, grid, stream);
-  else
-    e = a.D == 128 ? launch_score<float, 128>(a, grid, stream) : launch_score<float, 64>(a, grid, stream);
+    return a.D == 128 ? launch_score<uint16_t, 128>(a, grid, stream) : launch_score<uint16_t, 64>(a, grid, stream);
+  return a.D == 128 ? launch_score<float, 128>(a, grid, stream) : launch_score<float, 64>(a, grid, stream);
+}
+
+hipError_t launch_select(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) {
+  hipError_t e = launch_scores(a, dt, stream);
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)a.max_pages * sizeof(uint32_t);
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(kTopkThreads), lds, stream, a);

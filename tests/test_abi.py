@@ -62,6 +62,8 @@ def test_invalid_kv_rejected_everywhere(bad, code):
     assert lib.s3r_dense_verify_attn(kv, v, 5, 0.1, 0, v, v, 1 << 30, None) == code
     assert lib.s3r_attn_workspace(kv, 5, 8) == 0
     assert lib.s3r_page_select_workspace(kv, 64) == 0
+    assert lib.s3r_sparse_draft_step(kv, v, None, v, 64, 0.1, v, v, 0, v, v, 1 << 30, None) == code
+    assert lib.s3r_sparse_draft_step_workspace(kv, 64) == 0
 
 
 def test_invalid_call_arguments():
@@ -101,6 +103,14 @@ def test_invalid_call_arguments():
     sneed = lib.s3r_spec_sample_workspace(2, 4, 1024)
     assert sneed > 0 and lib.s3r_spec_sample_workspace(2, 17, 1024) == 0
     assert s(2, 4, 1024, v, v, v, 1.0, 0, 0, v, v, v, sneed - 1, None) == 3
+    d = lib.s3r_sparse_draft_step
+    assert d(kv, None, None, v, 64, 0.1, v, v, 0, v, v, big, None) == 1      # bounds
+    assert d(kv, v, None, v, 15, 0.1, v, v, 0, v, v, big, None) == 1        # budget < P
+    assert d(kv, v, None, v, 64, 0.1, None, v, 0, v, v, big, None) == 1     # selected
+    assert d(kv, v, None, v, 64, 0.1, v, v, 7, v, v, big, None) == 2        # out dtype
+    dneed = lib.s3r_sparse_draft_step_workspace(kv, 64)
+    assert dneed > 0  # the page scores
+    assert d(kv, v, None, v, 64, 0.1, v, v, 0, v, v, dneed - 1, None) == 3
 
 
 def test_split_plan_workspace_scales_with_hint():

@@ -2,9 +2,10 @@
 bench.py times (same split plan, same workspaces), checked on sampled
 (sequence, kv head) slices the oracle computes one by one.
 
-Per workload: the first draft step (tail-page bounds refresh, page select,
-sparse draft attention), the dense verify of gamma + 1 queries, and the
-speculative sampling of every sequence. Tolerances as in test_gpu_parity.py.
+Per workload: the first draft step (the fused tail-page bounds refresh, page
+select and sparse draft attention, as bench.py runs it), the dense verify of
+gamma + 1 queries, and the speculative sampling of every sequence. Tolerances
+as in test_gpu_parity.py.
 """
 import math
 
@@ -52,15 +53,13 @@ def _run_fullsize(name, samples, shrink_to=None):
     kv = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[0], Hq,
                           total_pages_hint=total)
     bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device="cuda")
-    # bounds as of the full pre-filled KV, then the draft step's tail refresh
+    # bounds as of the full pre-filled KV; the draft step refreshes its tail page
     kv.set_seq_lens(wl.seq_lens[gamma])
     s3r.page_bounds_update(kv, bounds)
     kv.set_seq_lens(wl.seq_lens[0])
-    s3r.page_bounds_update(kv, bounds, first_pos=(wl.seq_lens[0] - 1).contiguous(),
-                           max_pages_touched=1)
     q0 = wl.draft_q(0)
-    sel, nsel = s3r.page_select(kv, bounds, q0, budget, scale)
-    d_out = s3r.sparse_draft_attn(kv, q0, sel, scale)
+    d_out, sel, nsel = s3r.sparse_draft_step(kv, bounds, q0, budget, scale,
+                                             refresh_from=(wl.seq_lens[0] - 1).contiguous())
     kv.set_seq_lens(wl.seq_lens[gamma])
     v_out = s3r.dense_verify_attn(kv, wl.q_verify, scale)
     out, nacc = s3r.spec_sample(wl.draft_logits, wl.target_logits, wl.draft_tokens,

@@ -281,3 +281,46 @@ def test_edge_cases_empty_and_short():
     dr = s3r.sparse_draft_attn(kvc, wl.draft_q(0), sel, 0.1)
     torch.cuda.synchronize()
     assert np.all(dr[0].cpu().numpy() == 0)
+
+
+FUSED_CASES = [
+    ("bf16", 128, 4, 2, 64, (700, 300, 40)),
+    ("bf16", 128, 2, 2, 1024, (3000, 100)),    # selection longer than one workgroup's splits
+    ("bf16", 64, 8, 1, 48, (333, 15)),
+    ("bf16", 128, 4, 2, 4096, (100, 50)),      # budget covers every page
+    ("f32", 64, 2, 2, 64, (512, 300)),         # fp32: the separate kernels
+]
+
+
+@pytest.mark.parametrize("kv,D,G,Hkv,budget,ctx", FUSED_CASES)
+def test_fused_draft_step_equals_separate_calls(kv, D, G, Hkv, budget, ctx):
+    wl = _make(_cfg(kv, D, G, Hkv, budget=budget), list(ctx), seed=31)
+    scale = 1.0 / np.sqrt(D)
+    gamma = wl.cfg["gamma"]
+    # bounds as of the whole pre-filled KV: the step's tail page is stale until refreshed
+    stale = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(_kv(wl, gamma), stale)
+    for step in (0, 1, 3):
+        kvc = _kv(wl, step)
+        first = (wl.seq_lens[step] - 1).contiguous()
+        q = wl.draft_q(step)
+        ba = stale.clone()
+        s3r.page_bounds_update(kvc, ba, first_pos=first, max_pages_touched=1)
+        sel_a, n_a = s3r.page_select(kvc, ba, q, budget, scale)
+        out_a = s3r.sparse_draft_attn(kvc, q, sel_a, scale)
+        bb = stale.clone()
+        out_b, sel_b, n_b = s3r.sparse_draft_step(kvc, bb, q, budget, scale, refresh_from=first)
+        torch.cuda.synchronize()
+        assert torch.equal(ba, bb)
+        assert torch.equal(sel_a, sel_b) and torch.equal(n_a, n_b)
+        assert torch.equal(out_a, out_b)
+        # and against the oracle: bounds, selection (tie window) and attention
+        L = i32(wl.seq_lens[step])
+        rb = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), L)
+        used = ~np.isnan(rb[:, 0, 0, 0])
+        assert np.array_equal(f64(bb)[used], rb[used])
+        rsel, rn, rsc = oracle.page_select(rb, f64(q), i32(wl.page_table), L, budget, scale)
+        check_pages(i32(sel_b), i32(n_b), rsel, rn, rsc, budget // 16)
+        ref = oracle.sparse_draft_attn(f64(q), f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table),
+                                       L, i32(sel_b), scale)
+        _check_attn(out_b, ref, kv)
