@@ -117,8 +117,9 @@ s3r::SelectArgs select_args(const s3r_paged_kv* kv, const void* bounds, const vo
   return a;
 }
 
-// The fused draft step keeps the page keys, then the selection list, in LDS
-// beside the per-wave regions; it needs bf16 KV and at most 64 KB.
+// The fused draft step keeps the selection list in LDS after the per-wave
+// regions; it needs bf16 KV, at most 64 KB of LDS and a page table short
+// enough for its in-register top-k.
 struct DraftStepPlan {
   s3r::SplitPlan attn;
   size_t select_ws;
@@ -133,10 +134,10 @@ DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
   p.attn = s3r::plan_attention(kv, 1, k);
   p.select_ws = s3r::select_workspace_bytes(kv.num_seqs, kv.num_kv_heads, kv.max_pages_per_seq);
   const size_t regions = (size_t)p.attn.lds_region_bytes * p.attn.waves_per_group;
-  const size_t keys = sizeof(uint32_t) * (size_t)kv.max_pages_per_seq;
-  const size_t list_offset = ((regions > keys ? regions : keys) + 15) & ~(size_t)15;
+  const size_t list_offset = (regions + 15) & ~(size_t)15;
   p.list_offset = (int32_t)list_offset;
-  p.fused = kv.kv_dtype == S3R_BF16 && list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
+  p.fused = kv.kv_dtype == S3R_BF16 && kv.max_pages_per_seq <= s3r::kFusedTopkKeys * 64 * p.attn.waves_per_group &&
+            list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
   p.workspace_bytes = p.fused ? p.select_ws + p.attn.workspace_bytes
                               : (p.select_ws > p.attn.workspace_bytes ? p.select_ws : p.attn.workspace_bytes);
   return p;

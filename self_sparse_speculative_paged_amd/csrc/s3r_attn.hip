@@ -268,8 +268,8 @@ void attn_bf16_kernel(AttnArgs a) {
     int32_t* list = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(lds) + a.list_offset);
     const int k = a.ksel;
     if (k < n_pages)
-      block_topk<64 * kW>(a.scores + (size_t)bh * a.max_pages, n_pages, k,
-                          reinterpret_cast<uint32_t*>(lds), sh, list);
+      block_topk<64 * kW, kFusedTopkKeys>(a.scores + (size_t)bh * a.max_pages, n_pages, k, sh,
+                                          list);
     else
       for (int t = threadIdx.x; t < k; t += 64 * kW) list[t] = t < n_pages ? t : -1;
     __syncthreads();

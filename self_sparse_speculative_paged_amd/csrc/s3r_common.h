@@ -55,10 +55,52 @@ constexpr int kDppRowRor4 = 0x124;       // lane i <- lane (i + 4) mod 16 within
 constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7 - i within each 8-lane half
 constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppRowShr1 = 0x111;       // lane i <- lane i - 1 within its row (0 at the row start)
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;    // lane 15 of each row -> every lane of the next row
+constexpr int kDppRowBcast31 = 0x143;    // lane 31 -> every lane of rows 2 and 3
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Lanes that the row mask leaves out, or whose source lies outside the row, read 0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: a shift scan inside each
+// row of 16 lanes, then the row totals carried into the rows above.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<kDppRowShr1>(x);
+  x += dpp_u32<kDppRowShr2>(x);
+  x += dpp_u32<kDppRowShr4>(x);
+  x += dpp_u32<kDppRowShr8>(x);
+  x += dpp_u32<kDppRowBcast15, 0xA>(x);
+  x += dpp_u32<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+
+// Minimum (kMax false) or maximum of v over the wave, returned wave-uniform.
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return kMax ? max(a, b) : min(a, b); };
+  v = op(v, dpp_u32<kDppRowRor8>(v));
+  v = op(v, dpp_u32<kDppRowRor4>(v));
+  v = op(v, dpp_u32<kDppQuadXor2>(v));
+  v = op(v, dpp_u32<kDppQuadXor1>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
+// Number of set bits of a wave-wide mask below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Sum over aligned groups of kLanes (8 or 16) lanes; every lane gets its group's sum.

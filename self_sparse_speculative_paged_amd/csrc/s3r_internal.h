@@ -83,6 +83,10 @@ hipError_t launch_select(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t st
 hipError_t launch_scores(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
 size_t select_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_pages);
 int32_t select_max_pages_supported();
+// Page keys per thread of the fused draft step's in-register top-k: a kW-wave
+// workgroup ranks at most kFusedTopkKeys * 64 * kW pages per sequence; longer
+// page tables take the separate select kernel.
+constexpr int kFusedTopkKeys = 8;
 
 struct SampleArgs {
   const float* draft_logits;

@@ -19,7 +19,7 @@
 namespace s3r {
 namespace {
 
-constexpr int kMaxSelectPages = 12288;  // keys staged in LDS by the top-k pass
+constexpr int kMaxSelectPages = 12288;  // 12 keys per thread of the 1024-thread top-k block
 constexpr int kSelectPagesPerBlock = 128;  // pages scored by one 256-thread block
 
 // ---------------------------------------------------------------------------
@@ -300,7 +300,6 @@ constexpr int kTopkThreads = 1024;
 // One block per (sequence, kv head): the k best pages of its scores, ascending,
 // -1 padded; every page when k >= n.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
-  extern __shared__ uint32_t keys[];
   __shared__ TopkShared<kTopkThreads> sh;
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -314,7 +313,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
     for (int t = tid; t < k; t += kTopkThreads) out[t] = t < n ? t : -1;
     return;
   }
-  block_topk<kTopkThreads>(a.scores + (size_t)bh * a.max_pages, n, k, keys, sh, out);
+  block_topk<kTopkThreads, kMaxSelectPages / kTopkThreads>(a.scores + (size_t)bh * a.max_pages, n,
+                                                          k, sh, out);
 }
 
 template <typename T, int kD>
@@ -364,8 +364,7 @@ hipError_t launch_scores(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) 
 hipError_t launch_select(const SelectArgs& a, s3r_dtype dt, hipStream_t stream) {
   hipError_t e = launch_scores(a, dt, stream);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)a.max_pages * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(kTopkThreads), lds, stream, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -5,7 +5,14 @@
 // select of the k-th largest key, then a stable compaction in page order emits
 // them ascending. Ties on the threshold key keep the lowest page indices. Key
 // bits shared by every key (the common prefix of the block's min and max key)
-// are skipped; the rest are resolved kDigitBits per pass.
+// are skipped; the rest are resolved kTopkDigitBits per pass, stopping early
+// once the bin that holds the k-th key is taken whole.
+//
+// Keys stay in registers: thread t holds keys e * kThreads + t for e < kR, so
+// a block handles n <= kR * kThreads pages (the callers check this on the host).
+// Each radix pass costs one barrier: histograms rotate over three LDS buffers
+// (one counting, one being cleared, one still being read) and every wave finds
+// the digit itself with a DPP scan. The compaction takes one more barrier.
 #pragma once
 
 #include "s3r_common.h"
@@ -24,138 +31,152 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 template <int kThreads>
 struct TopkShared {
-  uint32_t hist[kTopkBins];
-  uint32_t wave_tot[kThreads / 64];
+  uint32_t hist[3][kTopkBins];
   uint32_t s_min[kThreads / 64], s_max[kThreads / 64];
-  uint32_t s_digit, s_krem;
 };
 
-// Exclusive prefix sum over the threads of a block (fixed order).
-template <int kThreads>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  __syncthreads();
-  return base + incl - v;
-}
+// Writes the k best of scores[0..n) (requires k < n <= kR * kThreads, n < 65536)
+// to out[0..k) in ascending page order. Every thread of the block calls it.
+template <int kThreads, int kR>
+__device__ void block_topk(const float* scores, int n, int k, TopkShared<kThreads>& sh,
+                           int32_t* out) {
+  constexpr int kWaves = kThreads / 64;
+  static_assert(kThreads % 64 == 0 && kWaves <= 16, "1 to 16 waves");
+  static_assert(kR * kWaves <= kTopkBins, "per-chunk wave counts fit one histogram buffer");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-// Writes the k best of scores[0..n) (requires k < n) to out[0..k) in ascending
-// page order. keys: LDS scratch of n words. Every thread of the block calls it.
-template <int kThreads>
-__device__ void block_topk(const float* scores, int n, int k, uint32_t* keys,
-                           TopkShared<kThreads>& sh, int32_t* out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t key[kR];
+#pragma unroll
+  for (int e = 0; e < kR; ++e) {
+    const int j = e * kThreads + tid;
+    key[e] = j < n ? order_key(scores[j]) : 0u;
+  }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  // Scores are loaded 8 per thread at a time, all in flight together.
-  for (int j0 = 0; j0 < n; j0 += 8 * kThreads) {
-    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + tid + kThreads * e;
-      v[e] = j < n ? scores[j] : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + tid + kThreads * e;
-      if (j < n) {
-        const uint32_t key = order_key(v[e]);
-        keys[j] = key;
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-      }
+  for (int e = 0; e < kR; ++e) {
+    if (e * kThreads + tid < n) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
     }
   }
-  for (int x = 32; x >= 1; x >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, x, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, x, 64));
-  }
+  kmin = wave_extreme_u32<false>(kmin);
+  kmax = wave_extreme_u32<true>(kmax);
   if (lane == 0) {
     sh.s_min[wave] = kmin;
     sh.s_max[wave] = kmax;
   }
-  for (int i = tid; i < kTopkBins; i += kThreads) sh.hist[i] = 0;
+  for (int i = tid; i < kTopkBins; i += kThreads) sh.hist[0][i] = 0;
   __syncthreads();
-  for (int w = 0; w < kThreads / 64; ++w) {
-    kmin = min(kmin, sh.s_min[w]);
-    kmax = max(kmax, sh.s_max[w]);
-  }
+  kmin = wave_extreme_u32<false>(lane < kWaves ? sh.s_min[lane] : 0xffffffffu);
+  kmax = wave_extreme_u32<true>(lane < kWaves ? sh.s_max[lane] : 0u);
+
+  // Invariant: the keys still in play are those with (key & mask) == prefix,
+  // and krem of them belong to the top k (every key above them does).
   const int varying = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));
-  uint32_t prefix = kmin & (varying >= 32 ? 0u : ~((1u << varying) - 1u));
   uint32_t mask = varying >= 32 ? 0u : ~((1u << varying) - 1u);
+  uint32_t prefix = kmin & mask;
   uint32_t krem = (uint32_t)k;
+  bool whole_bin = false;
+  int cur = 0;
   for (int lo_bit = varying - kTopkDigitBits; lo_bit > -kTopkDigitBits; lo_bit -= kTopkDigitBits) {
     const int shift = max(lo_bit, 0);
     const int width = lo_bit >= 0 ? kTopkDigitBits : kTopkDigitBits + lo_bit;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int j0 = 0; j0 < n; j0 += kThreads) {
-      const int j = j0 + tid;
-      const uint32_t key = j < n ? keys[j] : 0u;
-      if (j < n && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    uint32_t* hist = sh.hist[cur];
+    // The buffer cleared here was last read before the previous barrier.
+    for (int i = tid; i < kTopkBins; i += kThreads) sh.hist[nxt][i] = 0;
+#pragma unroll
+    for (int e = 0; e < kR; ++e) {
+      if (e * kThreads + tid < n && (key[e] & mask) == prefix)
+        atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      // Lane l holds the 8 bins 8l..8l+7 counted from the top digit down.
-      constexpr int kPer = kTopkBins / 64;
-      uint32_t cnt[kPer], own = 0;
+    // Lane l holds kPer consecutive bins counted from the top digit down; the
+    // one lane whose running count crosses krem names the digit.
+    constexpr int kPer = kTopkBins / 64;
+    uint32_t cnt[kPer], own = 0;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        cnt[e] = sh.hist[kTopkBins - 1 - (kPer * lane + e)];
-        own += cnt[e];
-      }
-      uint32_t incl = own;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-      }
-      uint32_t above = incl - own;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        if (above < krem && above + cnt[e] >= krem) {
-          sh.s_digit = (uint32_t)(kTopkBins - 1 - (kPer * lane + e));
-          sh.s_krem = krem - above;
-        }
-        above += cnt[e];
-      }
+    for (int e = 0; e < kPer; ++e) {
+      cnt[e] = hist[kTopkBins - 1 - (kPer * lane + e)];
+      own += cnt[e];
     }
-    __syncthreads();
-    prefix |= sh.s_digit << shift;
+    uint32_t above = wave_incl_scan(own) - own;
+    uint32_t hit_digit = 0, hit_krem = 0, hit_count = 0;
+    bool hit = false;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (above < krem && above + cnt[e] >= krem) {
+        hit = true;
+        hit_digit = (uint32_t)(kTopkBins - 1 - (kPer * lane + e));
+        hit_krem = krem - above;
+        hit_count = cnt[e];
+      }
+      above += cnt[e];
+    }
+    const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
+    const int src = hits ? __builtin_ctzll(hits) : 0;
+    prefix |= (uint32_t)__builtin_amdgcn_readlane(hit_digit, src) << shift;
     mask |= dmask << shift;
-    krem = sh.s_krem;
-    for (int i = tid; i < kTopkBins; i += kThreads) sh.hist[i] = 0;
-    __syncthreads();
+    krem = __builtin_amdgcn_readlane(hit_krem, src);
+    const uint32_t count = __builtin_amdgcn_readlane(hit_count, src);
+    cur = nxt;
+    // Every key of the chosen bin is taken: the bin's low end bounds the set.
+    if (count == krem) {
+      whole_bin = true;
+      break;
+    }
   }
-  const uint32_t thr = prefix;
+  // Taken: keys above thr, and the first krem keys (in page order) equal to
+  // thr. A whole bin taken at once becomes thr = its low end - 1, krem = 0;
+  // that low end is positive, since some key (k < n) lies below every taken one.
+  const uint32_t thr = whole_bin ? prefix - 1u : prefix;
+  if (whole_bin) krem = 0;
 
-  // Contiguous chunk per thread, scanned twice: equal-key ranks, then output slots.
-  const int chunk = (n + kThreads - 1) / kThreads;
-  const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
-  uint32_t n_eq = 0;
-  for (int j = lo; j < hi; ++j) n_eq += keys[j] == thr;
-  const uint32_t eq_before = block_exclusive_scan<kThreads>(n_eq, sh.wave_tot);
-  uint32_t n_take = 0, eq_rank = eq_before;
-  for (int j = lo; j < hi; ++j) {
-    const uint32_t key = keys[j];
-    if (key > thr) ++n_take;
-    else if (key == thr) n_take += (eq_rank++ < krem);
+  // Compaction. Per chunk and wave, (keys equal to thr) << 16 | (keys above
+  // it) goes to the buffer cleared in the last pass, which no wave reads any
+  // more; an exclusive scan of those words in (chunk, wave) order, plus the
+  // lanes below in the wave, gives gt(p) and eq(p), the keys above and equal
+  // to thr before position p. The key at p, if taken, lands at gt(p) + min(eq(p), krem).
+  uint32_t* wc = sh.hist[cur];
+  const int nchunks = (n + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int e = 0; e < kR; ++e) {
+    if (e < nchunks) {
+      const bool valid = e * kThreads + tid < n;
+      const uint64_t bg = __builtin_amdgcn_ballot_w64(valid && key[e] > thr);
+      const uint64_t be = __builtin_amdgcn_ballot_w64(valid && key[e] == thr);
+      if (lane == 0) wc[e * kWaves + wave] = (uint32_t)__popcll(be) << 16 | (uint32_t)__popcll(bg);
+    }
   }
-  const uint32_t slot0 = block_exclusive_scan<kThreads>(n_take, sh.wave_tot);
-  uint32_t slot = slot0;
-  eq_rank = eq_before;
-  for (int j = lo; j < hi; ++j) {
-    const uint32_t key = keys[j];
-    bool take = key > thr;
-    if (key == thr) take = (eq_rank++ < krem);
-    if (take && slot < (uint32_t)k) out[slot++] = j;
+  __syncthreads();
+  constexpr int kChunksPerScan = 64 / kWaves;
+  uint32_t carry = 0, v = 0, incl = 0;
+#pragma unroll
+  for (int e = 0; e < kR; ++e) {
+    if (e < nchunks) {
+      if (e % kChunksPerScan == 0) {
+        carry += __builtin_amdgcn_readlane(incl, 63);
+        const int idx = e * kWaves + lane;
+        v = idx < nchunks * kWaves ? wc[idx] : 0u;
+        incl = wave_incl_scan(v);
+      }
+      const int i = (e % kChunksPerScan) * kWaves + wave;
+      const uint32_t before =
+          carry + __builtin_amdgcn_readlane(incl, i) - __builtin_amdgcn_readlane(v, i);
+      const int j = e * kThreads + tid;
+      const bool valid = j < n;
+      const bool gt = valid && key[e] > thr, eq = valid && key[e] == thr;
+      const uint64_t bg = __builtin_amdgcn_ballot_w64(gt);
+      const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
+      const uint32_t gt_before = (before & 0xffffu) + lanes_below(bg);
+      const uint32_t eq_before = (before >> 16) + lanes_below(be);
+      if (gt || (eq && eq_before < krem)) {
+        const uint32_t slot = gt_before + min(eq_before, krem);
+        if (slot < (uint32_t)k) out[slot] = j;
+      }
+    }
   }
 }
 

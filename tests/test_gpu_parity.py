@@ -288,6 +288,8 @@ FUSED_CASES = [
     ("bf16", 128, 2, 2, 1024, (3000, 100)),    # selection longer than one workgroup's splits
     ("bf16", 64, 8, 1, 48, (333, 15)),
     ("bf16", 128, 4, 2, 4096, (100, 50)),      # budget covers every page
+    ("bf16", 64, 4, 2, 64, (8000, 7990)),      # one wave, eight key chunks per thread
+    ("bf16", 128, 4, 2, 64, (9000, 200)),      # too many pages for the fused top-k
     ("f32", 64, 2, 2, 64, (512, 300)),         # fp32: the separate kernels
 ]
 
