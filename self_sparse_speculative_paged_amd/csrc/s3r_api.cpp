@@ -3,6 +3,8 @@
 // contract of each entry point.
 #include <math.h>
 
+#include <atomic>
+
 #include "s3r.h"
 #include "s3r_internal.h"
 
@@ -125,7 +127,7 @@ struct DraftStepPlan {
   size_t select_ws;
   bool fused;
   int32_t list_offset;
-  size_t workspace_bytes;
+  size_t workspace_bytes;  // enough for every path the call may take
 };
 
 DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
@@ -140,6 +142,62 @@ DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
             list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
   p.workspace_bytes = p.fused ? p.select_ws + p.attn.workspace_bytes
                               : (p.select_ws > p.attn.workspace_bytes ? p.select_ws : p.attn.workspace_bytes);
+  return p;
+}
+
+// Compute units of the current device, cached per device (256 if the query fails).
+int32_t device_cu_count() {
+  static std::atomic<int32_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int32_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    int n = 0;
+    v = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Single-kernel draft step: one 8-wave workgroup per (sequence, kv head) that
+// scores, ranks and attends. It pays off when those workgroups fill the
+// device; each reads its whole bounds row, so it needs the row's page ids,
+// its scores and the list in LDS and its keys in the top-k's registers.
+struct SingleKernelPlan {
+  bool ok;
+  s3r::SplitPlan attn;
+  int32_t pt_offset, list_offset;
+};
+
+SingleKernelPlan plan_single_kernel(const s3r_paged_kv& kv, int32_t k) {
+  constexpr int kWaves = 8;
+  SingleKernelPlan p{};
+  const int32_t G = kv.num_q_heads / kv.num_kv_heads;
+  if (kv.kv_dtype != S3R_BF16 || (G != 1 && G != 2 && G != 4 && G != 8)) return p;
+  if (kv.max_pages_per_seq > s3r::kFusedTopkKeys * 64 * kWaves) return p;
+  if ((int64_t)kv.num_seqs * kv.num_kv_heads < device_cu_count()) return p;
+  s3r::SplitPlan& a = p.attn;
+  a.rows = G;
+  a.row_blocks = 1;
+  int32_t pps = (k + kWaves - 1) / kWaves;
+  pps = pps < 2 ? 2 : (pps + 1) & ~1;
+  a.pages_per_split = pps;
+  a.n_splits = (k + pps - 1) / pps;
+  a.waves_per_group = kWaves;
+  a.n_groups = 1;
+  const size_t table = sizeof(int) * 4 * (size_t)((pps + 1) / 2);
+  const size_t partial = sizeof(float) * (size_t)G * (kv.head_dim + 2);
+  a.lds_region_bytes = (int32_t)(((table > partial ? table : partial) + 15) & ~(size_t)15);
+  a.workspace_bytes = 0;
+  const size_t row = sizeof(int32_t) * (size_t)kv.max_pages_per_seq;
+  size_t front = (size_t)a.lds_region_bytes * kWaves;
+  if (front < row) front = row;  // the scores alias the wave regions
+  front = (front + 15) & ~(size_t)15;
+  const size_t list = (front + row + 15) & ~(size_t)15;
+  if (list + sizeof(int32_t) * (size_t)k > 64 * 1024) return p;
+  p.pt_offset = (int32_t)front;
+  p.list_offset = (int32_t)list;
+  p.ok = true;
   return p;
 }
 
@@ -227,6 +285,20 @@ s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int
   const int32_t k = budget_tokens / kv->page_size;
   s3r::SelectArgs sa = select_args(kv, bounds, q, budget_tokens, softmax_scale, selected,
                                    num_selected, workspace);
+  const SingleKernelPlan one = plan_single_kernel(*kv, k);
+  if (one.ok) {
+    s3r::AttnArgs a = attn_args(kv, one.attn, q, nullptr, k, 1, softmax_scale, out_dtype, out, nullptr);
+    a.sel_out = selected;
+    a.nsel_out = num_selected;
+    a.list_offset = one.list_offset;
+    a.score_here = 1;
+    a.pt_offset = one.pt_offset;
+    a.bounds = bounds;
+    a.bounds_out = bounds;
+    a.refresh_from = refresh_from;
+    a.sel_scale = softmax_scale;
+    return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
+  }
   if (plan.fused) {
     sa.refresh_from = refresh_from;
     sa.bounds_out = bounds;

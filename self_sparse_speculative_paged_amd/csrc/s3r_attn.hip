@@ -23,6 +23,7 @@
 // per window.
 #include "s3r_common.h"
 #include "s3r_internal.h"
+#include "s3r_score.h"
 #include "s3r_topk.h"
 
 namespace s3r {
@@ -232,17 +233,94 @@ constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : 2); }
 template <int kNB>
 constexpr int bf16_waves_per_simd() { return kNB == 1 ? 2 : 1; }
 
+// How a sparse workgroup gets its selection row.
+constexpr int kSelGiven = 0;       // a.sel, written by s3r_page_select
+constexpr int kSelFromScores = 1;  // top-k of the page scores in a.scores
+constexpr int kSelScoreHere = 2;   // score every page here, then top-k
+
+// Scores every page of (sequence b, kv head h) into sc[] (LDS) and copies its
+// page ids into pt_lds[]; pages from the refresh point on first get their
+// bounds recomputed from K and written back. score == false (every page is
+// taken) skips the bounds reads but still refreshes and copies the ids.
+template <int kD, int kG, int kThreads>
+__device__ __forceinline__ void score_row_to_lds(const AttnArgs& a, int b, int h, int seq_len,
+                                                 int n, bool score, float* sc, int32_t* pt_lds) {
+  constexpr int kLpp = kD / 8;
+  constexpr int kGroups = kThreads / kLpp;  // pages per block-wide step
+  constexpr int kIter = 8;                  // pages per page group per batch
+  constexpr int kBatch = kGroups * kIter;
+  const int c = threadIdx.x % kLpp, grp = threadIdx.x / kLpp;
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  const int rf = a.refresh_from ? min(max(a.refresh_from[b], 0) / kPage, n) : n;
+  PageScorerBf16<kD, kG> qs;
+  qs.load(static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h * kG) * kD, c);
+  // Refreshed pages (normally just the tail page) first, so their dependent
+  // K loads overlap the first batch.
+  for (int j = rf + grp; j < n; j += kGroups) {
+    const int phys = pt[j];
+    uint4 lo, hi;
+    refresh_page_bounds_bf16<kD>(static_cast<const uint16_t*>(a.k_pool),
+                                 static_cast<uint16_t*>(a.bounds_out), a.Hkv, h, phys,
+                                 min(kPage, seq_len - kPage * j), c, lo, hi);
+    if (score) {
+      const float s = qs.score(lo, hi, a.sel_scale);
+      if (c == 0) sc[j] = s;
+    }
+    if (c == 1) pt_lds[j] = phys;
+  }
+  // Pages before the refresh point in batches of kIter per page group; the
+  // next batch's page ids load while this batch's bounds are scored.
+  const uint16_t* bb = static_cast<const uint16_t*>(a.bounds);
+  int ids[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int j = grp + kGroups * i;
+    ids[i] = j < rf ? pt[j] : -1;
+  }
+  for (int base = 0; base < rf; base += kBatch) {
+    int cur[kIter];
+    uint4 lo[kIter], hi[kIter];
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      cur[i] = ids[i];
+      if (score && cur[i] >= 0) {
+        const uint16_t* pb = bb + ((size_t)cur[i] * a.Hkv + h) * 2 * kD + 8 * c;
+        lo[i] = load_nt16<uint4>(pb);
+        hi[i] = load_nt16<uint4>(pb + kD);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int j = base + kBatch + grp + kGroups * i;
+      ids[i] = j < rf ? pt[j] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      if (cur[i] < 0) continue;  // uniform within the page group
+      const int j = base + grp + kGroups * i;
+      if (score) {
+        const float s = qs.score(lo[i], hi[i], a.sel_scale);
+        if (c == 0) sc[j] = s;
+      }
+      if (c == 1) pt_lds[j] = cur[i];
+    }
+  }
+}
+
 // Each wave of a kW-wave workgroup owns one split of the same (sequence, kv
 // head). Its LDS region holds first its window table, then (once its pipeline
 // has drained) its (m, l, o) partial; after a barrier the workgroup merges the
 // kW partials and writes either the final output (one group per (sequence,
 // head)) or one group partial for the global combine.
 //
-// kSelect (the fused draft step): the workgroup first selects its (sequence,
-// kv head)'s pages itself, by an exact block top-k over the page scores in
-// LDS, and attends over that list; group 0 also writes the list and the count
-// out, as s3r_page_select would.
-template <int kD, int kNB, bool kSparse, int kW, bool kSelect = false>
+// kSelect != kSelGiven (the fused draft step): the workgroup first selects its
+// (sequence, kv head)'s pages itself, by an exact block top-k over the page
+// scores, and attends over that list in LDS; group 0 also writes the list and
+// the count out, as s3r_page_select would. With kSelScoreHere the scores come
+// from this workgroup too (kG q heads per kv head, one group per (sequence,
+// kv head)): LDS then holds the scores over the wave regions (dead once the
+// top-k has read them), the page-table row at pt_offset and the list.
+template <int kD, int kNB, bool kSparse, int kW, int kSelect = kSelGiven, int kG = 0>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(bf16_waves_per_simd<kNB>(), 8)))
 void attn_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
@@ -255,7 +333,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
   const int g0 = group * kW * a.pages_per_split;
   // the global combine skips an empty group (group 0 still publishes the selection)
-  if (g0 >= n_items && a.n_groups > 1 && !(kSelect && group == 0)) return;
+  if (g0 >= n_items && a.n_groups > 1 && !(kSelect != kSelGiven && group == 0)) return;
   const int j0 = g0 + wave * a.pages_per_split;
   const int j1 = min(j0 + a.pages_per_split, n_items);
   const bool active = j0 < n_items;
@@ -263,13 +341,23 @@ void attn_bf16_kernel(AttnArgs a) {
   extern __shared__ int4 lds[];
   char* region = reinterpret_cast<char*>(lds) + (size_t)wave * a.lds_region_bytes;
   const int32_t* sel_row = kSparse ? a.sel + ((size_t)b * a.Hkv + h) * a.ksel : nullptr;
-  if constexpr (kSelect) {
+  const int32_t* pt_row = a.page_table + (size_t)b * a.max_pages;
+  if constexpr (kSelect != kSelGiven) {
     __shared__ TopkShared<64 * kW> sh;
-    int32_t* list = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(lds) + a.list_offset);
+    char* lds_bytes = reinterpret_cast<char*>(lds);
+    int32_t* list = reinterpret_cast<int32_t*>(lds_bytes + a.list_offset);
     const int k = a.ksel;
+    const float* scores = a.scores + (size_t)bh * a.max_pages;
+    if constexpr (kSelect == kSelScoreHere) {
+      int32_t* pt_lds = reinterpret_cast<int32_t*>(lds_bytes + a.pt_offset);
+      float* sc = reinterpret_cast<float*>(lds_bytes);
+      score_row_to_lds<kD, kG, 64 * kW>(a, b, h, seq_len, n_pages, k < n_pages, sc, pt_lds);
+      __syncthreads();
+      scores = sc;
+      pt_row = pt_lds;
+    }
     if (k < n_pages)
-      block_topk<64 * kW, kFusedTopkKeys>(a.scores + (size_t)bh * a.max_pages, n_pages, k, sh,
-                                          list);
+      block_topk<64 * kW, kFusedTopkKeys>(scores, n_pages, k, sh, list);
     else
       for (int t = threadIdx.x; t < k; t += 64 * kW) list[t] = t < n_pages ? t : -1;
     __syncthreads();
@@ -294,7 +382,7 @@ void attn_bf16_kernel(AttnArgs a) {
   if (active) {
     const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
-    const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+    const int32_t* pt = pt_row;
     const int32_t* sel = sel_row;
     const uint16_t* qg = static_cast<const uint16_t*>(a.q);
 
@@ -597,11 +685,22 @@ template <int kD>
 hipError_t launch_fused_draft(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_groups));
   const size_t lds = (size_t)a.list_offset + sizeof(int32_t) * a.ksel;
+  if (a.score_here) {  // one group of 8 waves per (sequence, kv head)
+    if (a.waves_per_group != 8 || a.n_groups != 1) return hipErrorInvalidValue;
+    switch (a.G) {
+      case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 1>), grid, dim3(512), lds, stream, a); break;
+      case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 2>), grid, dim3(512), lds, stream, a); break;
+      case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 4>), grid, dim3(512), lds, stream, a); break;
+      case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 8>), grid, dim3(512), lds, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.waves_per_group) {
-    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 1, true>), grid, dim3(64), lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 2, true>), grid, dim3(128), lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 4, true>), grid, dim3(256), lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, true>), grid, dim3(512), lds, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 1, kSelFromScores>), grid, dim3(64), lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 2, kSelFromScores>), grid, dim3(128), lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 4, kSelFromScores>), grid, dim3(256), lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelFromScores>), grid, dim3(512), lds, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -670,7 +769,7 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
 }
 
 hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream) {
-  if (a.scores != nullptr) {  // fused draft step: bf16, one row block
+  if (a.scores != nullptr || a.score_here) {  // fused draft step: bf16, one row block
     if (kv_dtype != S3R_BF16 || a.rows > 16) return hipErrorInvalidValue;
     return a.D == 128 ? launch_fused_draft<128>(a, stream) : launch_fused_draft<64>(a, stream);
   }

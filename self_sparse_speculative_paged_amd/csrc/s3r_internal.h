@@ -47,6 +47,15 @@ struct AttnArgs {
   int32_t* sel_out;
   int32_t* nsel_out;
   int32_t list_offset;
+  // Single-kernel draft step (score_here != 0): the workgroup scores its pages
+  // from the bf16 bounds (refreshing pages from refresh_from[b] / P on into
+  // bounds_out) with sel_scale, keeping its page-table row in LDS at pt_offset.
+  int32_t score_here;
+  int32_t pt_offset;
+  const void* bounds;
+  void* bounds_out;
+  const int32_t* refresh_from;
+  float sel_scale;
 };
 
 hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream);

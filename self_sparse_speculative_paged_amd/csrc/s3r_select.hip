@@ -14,6 +14,7 @@
 // vectors: for bf16 bounds, v_dot2_f32_bf16 on the packed bounds as loaded.
 #include "s3r_common.h"
 #include "s3r_internal.h"
+#include "s3r_score.h"
 #include "s3r_topk.h"
 
 namespace s3r {
@@ -108,57 +109,6 @@ __global__ __launch_bounds__(64) void bounds_kernel(BoundsArgs a) {
   }
 }
 
-// Recomputes the bf16 bounds of page j of (sequence b, kv head h) from K over
-// its valid tokens, writes them to the bounds buffer and returns them packed as
-// loaded: lane c of the page group owns d = 8c .. 8c+7.
-template <int kD>
-__device__ __forceinline__ void refresh_page_bounds(const SelectArgs& a, int b, int h, int j,
-                                                    int seq_len, int phys, int c, uint4& kmin,
-                                                    uint4& kmax) {
-  const int valid = min(kPage, seq_len - kPage * j);
-  const uint16_t* kb =
-      static_cast<const uint16_t*>(a.k_pool) + ((size_t)phys * a.Hkv + h) * kPage * kD + 8 * c;
-  float mn[8], mx[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mn[e] = __builtin_huge_valf();
-    mx[e] = -__builtin_huge_valf();
-  }
-  // Two halves of 8 rows: each half's loads are in flight together.
-#pragma unroll
-  for (int t0 = 0; t0 < kPage; t0 += kPage / 2) {
-    uint4 rows[kPage / 2];
-#pragma unroll
-    for (int t = 0; t < kPage / 2; ++t)
-      rows[t] = *reinterpret_cast<const uint4*>(kb + (size_t)(t0 + t < valid ? t0 + t : 0) * kD);
-#pragma unroll
-    for (int t = 0; t < kPage / 2; ++t) {
-      if (t0 + t < valid) {
-        const uint32_t w[4] = {rows[t].x, rows[t].y, rows[t].z, rows[t].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
-          mn[2 * e] = fminf(mn[2 * e], lo);
-          mx[2 * e] = fmaxf(mx[2 * e], lo);
-          mn[2 * e + 1] = fminf(mn[2 * e + 1], hi);
-          mx[2 * e + 1] = fmaxf(mx[2 * e + 1], hi);
-        }
-      }
-    }
-  }
-  uint32_t pmn[4], pmx[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    pmn[e] = (uint32_t)f32_to_bf16_bits(mn[2 * e]) | ((uint32_t)f32_to_bf16_bits(mn[2 * e + 1]) << 16);
-    pmx[e] = (uint32_t)f32_to_bf16_bits(mx[2 * e]) | ((uint32_t)f32_to_bf16_bits(mx[2 * e + 1]) << 16);
-  }
-  kmin = make_uint4(pmn[0], pmn[1], pmn[2], pmn[3]);
-  kmax = make_uint4(pmx[0], pmx[1], pmx[2], pmx[3]);
-  uint16_t* pb = static_cast<uint16_t*>(a.bounds_out) + ((size_t)phys * a.Hkv + h) * 2 * kD + 8 * c;
-  *reinterpret_cast<uint4*>(pb) = kmin;
-  *reinterpret_cast<uint4*>(pb + kD) = kmax;
-}
-
 // ---------------------------------------------------------------------------
 // Scores: a group of D/8 lanes scores one page for every q head of the kv
 // head; a wave scores 64/(D/8) pages per step.
@@ -192,36 +142,9 @@ void score_kernel(SelectArgs a) {
   }
 
   if constexpr (sizeof(T) == 2) {
-    bf16x2 qp[kG][4], qn[kG][4];
-    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h * kG) * kD + 8 * c;
-#pragma unroll
-    for (int g = 0; g < kG; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t bits = qg[(size_t)g * kD + e];
-        const bool neg = (bits & 0x8000u) != 0;
-        const __bf16 v = __builtin_bit_cast(__bf16, bits);
-        const __bf16 z = __builtin_bit_cast(__bf16, (uint16_t)0);
-        qp[g][e / 2][e % 2] = neg ? z : v;
-        qn[g][e / 2][e % 2] = neg ? v : z;
-      }
+    PageScorerBf16<kD, kG> qs;
+    qs.load(static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h * kG) * kD, c);
     const uint16_t* bb = static_cast<const uint16_t*>(a.bounds);
-    auto score_of = [&](const uint4& lo, const uint4& hi) {
-      const uint32_t mn[4] = {lo.x, lo.y, lo.z, lo.w};
-      const uint32_t mx[4] = {hi.x, hi.y, hi.z, hi.w};
-      float best = -__builtin_huge_valf();
-#pragma unroll
-      for (int g = 0; g < kG; ++g) {
-        float acc = 0.f;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          acc = __builtin_amdgcn_fdot2_f32_bf16(qp[g][p], __builtin_bit_cast(bf16x2, mx[p]), acc, false);
-          acc = __builtin_amdgcn_fdot2_f32_bf16(qn[g][p], __builtin_bit_cast(bf16x2, mn[p]), acc, false);
-        }
-        best = fmaxf(best, group_sum<kLpp>(acc));
-      }
-      return best * a.scale;
-    };
     // Pages before the refresh point: all bounds loads in flight together.
     uint4 kmin[kIter], kmax[kIter];
 #pragma unroll
@@ -238,7 +161,7 @@ void score_kernel(SelectArgs a) {
       for (int i = 0; i < kIter; ++i) {
         const int j = start + grp + kGroups * i;
         if (phys[i] < 0 || j >= rf) continue;  // uniform within the page group
-        const float sc = score_of(kmin[i], kmax[i]);
+        const float sc = qs.score(kmin[i], kmax[i], a.scale);
         if (c == 0) scores[j] = sc;
       }
     }
@@ -250,9 +173,11 @@ void score_kernel(SelectArgs a) {
         const int j = start + grp + kGroups * i;
         if (phys[i] < 0 || j < rf) continue;
         uint4 lo, hi;
-        refresh_page_bounds<kD>(a, b, h, j, seq_len, phys[i], c, lo, hi);
+        refresh_page_bounds_bf16<kD>(static_cast<const uint16_t*>(a.k_pool),
+                                     static_cast<uint16_t*>(a.bounds_out), a.Hkv, h, phys[i],
+                                     min(kPage, seq_len - kPage * j), c, lo, hi);
         if (score) {
-          const float sc = score_of(lo, hi);
+          const float sc = qs.score(lo, hi, a.scale);
           if (c == 0) scores[j] = sc;
         }
       }

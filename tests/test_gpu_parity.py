@@ -290,6 +290,11 @@ FUSED_CASES = [
     ("bf16", 128, 4, 2, 4096, (100, 50)),      # budget covers every page
     ("bf16", 64, 4, 2, 64, (8000, 7990)),      # one wave, eight key chunks per thread
     ("bf16", 128, 4, 2, 64, (9000, 200)),      # too many pages for the fused top-k
+    # 32 sequences x 8 kv heads fill the device: the single-kernel step (scores
+    # in LDS); ragged lengths, some short enough that every page is taken
+    ("bf16", 128, 4, 8, 512, tuple(60 + 97 * i for i in range(32))),
+    ("bf16", 64, 8, 8, 256, tuple(3000 - 90 * i for i in range(32))),
+    ("bf16", 128, 1, 8, 2048, tuple(2100 + 61 * i for i in range(32))),
     ("f32", 64, 2, 2, 64, (512, 300)),         # fp32: the separate kernels
 ]
 
@@ -315,7 +320,8 @@ def test_fused_draft_step_equals_separate_calls(kv, D, G, Hkv, budget, ctx):
         torch.cuda.synchronize()
         assert torch.equal(ba, bb)
         assert torch.equal(sel_a, sel_b) and torch.equal(n_a, n_b)
-        assert torch.equal(out_a, out_b)
+        # the same pages and arithmetic; only the split-KV merge order may differ
+        torch.testing.assert_close(out_b, out_a, rtol=1e-5, atol=1e-5)
         # and against the oracle: bounds, selection (tie window) and attention
         L = i32(wl.seq_lens[step])
         rb = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), L)
