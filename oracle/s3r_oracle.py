@@ -53,7 +53,7 @@ __all__ = [
     "PHILOX_M0", "PHILOX_M1", "PHILOX_W0", "PHILOX_W1",
     "philox4x64_10", "uniform",
     "key_row", "value_row", "n_pages",
-    "page_bounds", "page_scores", "page_select",
+    "page_bounds", "page_scores", "page_select", "round_forced_pages", "page_select_round",
     "attend", "sparse_draft_attn", "dense_verify_attn", "decode_streaming",
     "softmax", "icdf", "spec_sample", "draw_draft_tokens",
 ]
@@ -190,6 +190,63 @@ def page_select(bounds, q, page_table, seq_lens, budget_tokens, scale, P=16, seq
             order = sorted(range(n), key=lambda j: (-sc[j], j))
             selected[b, h, :] = sorted(order[:k])
             scores[(b, h)] = sc
+    return selected, num_selected, scores
+
+
+def round_forced_pages(seq_len, gamma, P, max_pages):
+    """Logical pages holding the positions of one round's gamma draft queries.
+
+    Draft step j of a round queries position seq_len - 1 + j (seq_len is the
+    length at step 0), so the round's queries sit at positions
+    max(seq_len - 1, 0) .. seq_len + gamma - 2; their pages, below max_pages,
+    ascending. With gamma <= P that is one or two pages.
+    """
+    lo, hi = max(seq_len - 1, 0), seq_len + gamma - 2
+    return sorted({p // P for p in range(lo, hi + 1) if p // P < max_pages})
+
+
+def page_select_round(bounds, q, page_table, seq_lens, budget_tokens, gamma, scale, P=16,
+                      seqs=None):
+    """Once-per-round selection: the round's forced tail pages plus the best rest.
+
+    Selection-frequency variant of page_select (a reading of the pages: they do
+    not say how often drafting re-selects). Made once at draft step 0 and
+    reused by the round's later steps, it must keep the pages the later queries
+    sit in, which may not exist yet at step 0: every page of
+    round_forced_pages(seq_len, gamma, ...) is kept, and the remaining
+    k - |forced| slots go to the other existing pages ranked as in page_select
+    (score descending, index ascending), or to all of them if they fit. Output
+    ascending, -1 padded; num_selected[b] counts the kept pages. Requires
+    k >= |forced|.
+
+    Returns (selected[B][Hkv][k], num_selected[B], scores) with scores[(b, h)]
+    the candidate pages' scores (None when every candidate is kept).
+    """
+    B, max_pages = page_table.shape
+    hkv = bounds.shape[1]
+    k = budget_tokens // P
+    selected = np.full((B, hkv, k), -1, dtype=np.int32)
+    num_selected = np.zeros(B, dtype=np.int32)
+    scores = {}
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        n = n_pages(L, P)
+        forced = round_forced_pages(L, gamma, P, max_pages)
+        if k < len(forced):
+            raise ValueError("budget smaller than the round's forced pages")
+        candidates = [j for j in range(n) if j not in forced]
+        rest = k - len(forced)
+        for h in range(hkv):
+            if rest >= len(candidates):
+                chosen = candidates
+                scores[(b, h)] = None
+            else:
+                sc = page_scores(bounds, q, page_table, seq_lens, scale, b, h, P)
+                chosen = sorted(candidates, key=lambda j: (-sc[j], j))[:rest]
+                scores[(b, h)] = {j: sc[j] for j in candidates}
+            kept = sorted(set(forced) | set(chosen))
+            selected[b, h, :len(kept)] = kept
+            num_selected[b] = len(kept)
     return selected, num_selected, scores
 
 
