@@ -3,11 +3,11 @@
  * MI355X (gfx950).
  *
  * "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
- * Abstract: a rollout round drafts tokens with sparse attention, then produces
- * the response through full-attention verification and exact speculative
- * sampling; draft and verify share one set of policy parameters, so both read
- * the same KV cache, and dense verification reads the complete KV history.
- * The calls below are that round's per-step operations.
+ * Abstract: in one rollout round the policy proposes tokens while attending to
+ * only part of its KV cache; a dense pass over every cached key and value then
+ * checks them, and speculative sampling accepts or resamples so that the output
+ * keeps the dense policy's distribution. Drafter and verifier are one model, so
+ * they share one cache. The calls below are that round's per-step operations.
  *
  * Conventions for every call
  * --------------------------
@@ -123,7 +123,7 @@ s3r_status s3r_page_select(const s3r_paged_kv* kv, const void* bounds, const voi
 
 /*
  * s3r_sparse_draft_attn: one draft step's attention, over the selected pages
- * only ("uses sparse attention to propose tokens", S3R Abstract). Query head g
+ * only (S3R Abstract: the drafter is the policy itself, attending sparsely). Query head g
  * of sequence b attends, with softmax(softmax_scale * q K^T) V, to the tokens
  * t < seq_len of the pages in selected[b][g / G]. The G heads of a kv head
  * share each K/V tile they read.
@@ -139,18 +139,19 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const in
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * s3r_sparse_draft_step: one whole draft step in two kernel launches, the
- * fused form of
+ * s3r_sparse_draft_step: one whole draft step, the fused form of
  *   s3r_page_bounds_update(refresh_from)  (when refresh_from is not NULL)
  *   s3r_page_select(q, budget_tokens)     -> selected, num_selected
  *   s3r_sparse_draft_attn(q, selected)    -> out
- * with identical results. The score pass refreshes the bounds of pages from
- * refresh_from[b] / P to the tail (writing them to `bounds`) as it scores them;
- * each attention workgroup then selects its (sequence, kv head)'s pages by the
- * same exact top-k, in LDS, and attends over them. fp32 KV (and selections too
- * large for LDS) run the three calls' kernels instead.
+ * The bounds written and the selection are identical to those calls'; the
+ * attention output equals theirs up to the order in which split partials are
+ * merged. bf16 KV runs one kernel when one workgroup per (sequence, kv head)
+ * fills the device (it refreshes, scores, ranks in LDS and attends), else two
+ * (scores with the refresh, then rank-and-attend); fp32 KV and very long page
+ * tables run the three calls' kernels.
  *   bounds        in/out, [num_phys_pages][Hkv][2][D] kv dtype.
- *   refresh_from  [B] int32 or NULL.
+ *   refresh_from  [B] int32 or NULL: pages from refresh_from[b] / P to the
+ *                 tail get their bounds recomputed from K first.
  *   selected, num_selected: out, as s3r_page_select.   out: as s3r_sparse_draft_attn.
  * Errors: as the three calls; WORKSPACE_TOO_SMALL if workspace_bytes <
  * s3r_sparse_draft_step_workspace().
@@ -162,10 +163,33 @@ s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int
                                  void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * s3r_dense_verify_attn: full-attention verification of the draft ("dense
- * verification still requires the complete historical KV cache", S3R
- * Abstract). Query i = 0..n_q-1 of sequence b sits at position
- * seq_len - n_q + i and attends causally to every position <= its own, over
+ * s3r_sparse_draft_round: draft step 0 of a round whose selection is made
+ * once and reused by the round's later steps (a selection-frequency variant of
+ * re-selecting at every step; the S3R abstract leaves the frequency open).
+ * As s3r_sparse_draft_step, except the selection: with seq_len the step-0
+ * length, the logical pages holding positions seq_len - 1 .. seq_len + gamma - 2
+ * (where the round's gamma draft queries sit; one or two pages, clipped to
+ * max_pages_per_seq) are always kept, including one that does not exist yet,
+ * and the other k - |forced| slots go to the best-scoring remaining pages (all
+ * of them if they fit). Rows are ascending and -1 padded; num_selected[b]
+ * counts the kept pages. Draft step j > 0 then calls s3r_sparse_draft_attn
+ * with the same `selected` and its own seq_lens (pages past the sequence are
+ * masked until they fill).
+ *   gamma  1..16, the round's draft length.
+ * Errors: INVALID_ARGUMENT if gamma is out of range or budget_tokens < 2 * P;
+ * otherwise as s3r_sparse_draft_step, whose workspace query applies.
+ */
+s3r_status s3r_sparse_draft_round(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
+                                  const void* q, int32_t budget_tokens, int32_t gamma,
+                                  float softmax_scale, int32_t* selected, int32_t* num_selected,
+                                  s3r_dtype out_dtype, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_dense_verify_attn: full-attention verification of the draft (S3R
+ * Abstract: verifying reads every cached key and value of the sequence).
+ * Query i = 0..n_q-1 of sequence b sits at position seq_len - n_q + i and
+ * attends causally to every position <= its own, over
  * all pages of the sequence. n_q = gamma + 1 (the last committed token plus
  * the gamma drafts) gives the gamma + 1 target distributions of one round.
  *   q    [B][n_q][Hq][D] kv dtype.

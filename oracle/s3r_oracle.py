@@ -7,11 +7,12 @@ It shares no code with the HIP path.
 What is computed, and where it comes from
 -----------------------------------------
 "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
-Abstract: tokens are drafted with *sparse attention*, the response is produced by
-*full-attention verification* and *exact speculative sampling*, draft and verify
-share one set of parameters (so one KV cache serves both), and dense
-verification needs the *complete* KV history. The pages give no equations, so
-every step below is the plain definition of the operation, written out:
+Abstract: the policy drafts while attending to part of its KV cache, a dense
+attention pass over the whole cached history checks the draft, and speculative
+sampling keeps the output distributed as the dense policy's; drafter and
+verifier are one model, so one KV cache serves both. The pages give no
+equations, so every step below is the plain definition of the operation,
+written out:
 
 * page bounds / page select: the pages leave the sparse rule open; this library
   fixes a query-aware rule after the Quest title the page-3 reference list

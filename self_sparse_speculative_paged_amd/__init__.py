@@ -8,7 +8,8 @@ in (pre-allocated, e.g. for timing or graph capture) or are allocated here.
 
 Entry points (same names as include/s3r.h without the prefix):
   page_bounds_update, page_select, sparse_draft_attn, sparse_draft_step (the
-  three fused), dense_verify_attn, spec_sample, and the workspace queries.
+  three fused), sparse_draft_round (a draft step whose selection the round's
+  later steps reuse), dense_verify_attn, spec_sample, and the workspace queries.
 """
 import ctypes
 
@@ -21,6 +22,7 @@ __all__ = [
     "S3RError", "PagedKVCache", "page_bounds_update", "page_select", "sparse_draft_attn",
     "dense_verify_attn", "spec_sample", "page_select_workspace", "attn_workspace",
     "spec_sample_workspace", "version", "sparse_draft_step", "sparse_draft_step_workspace",
+    "sparse_draft_round",
 ]
 
 _KV_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
@@ -192,6 +194,34 @@ def sparse_draft_step(kv, bounds, q, budget_tokens, scale, refresh_from=None, se
         _dev(num_selected, "num_selected", torch.int32, (kv.B,)), _OUT_DTYPES[out.dtype],
         _dev(out, "out", None, (kv.B, kv.num_q_heads, kv.D)), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(stream)), "s3r_sparse_draft_step")
+    return out, selected, num_selected
+
+
+def sparse_draft_round(kv, bounds, q, budget_tokens, gamma, scale, refresh_from=None,
+                       selected=None, num_selected=None, out=None, out_dtype=torch.float32,
+                       workspace=None, stream=None):
+    """Draft step 0 of a round that selects once: the pages holding the round's
+    gamma query positions are always kept, the rest by score; later steps pass
+    the returned selection to sparse_draft_attn. Returns (out, selected,
+    num_selected); the workspace is sized by sparse_draft_step_workspace."""
+    lib = _lib.load()
+    k = budget_tokens // kv.P
+    if selected is None:
+        selected = torch.empty((kv.B, kv.Hkv, k), dtype=torch.int32, device=q.device)
+    if num_selected is None:
+        num_selected = torch.empty((kv.B,), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((kv.B, kv.num_q_heads, kv.D), dtype=out_dtype, device=q.device)
+    ws = _workspace(sparse_draft_step_workspace(kv, budget_tokens), q, workspace)
+    n_phys = kv.k_pool.shape[0]
+    rf = None if refresh_from is None else _dev(refresh_from, "refresh_from", torch.int32, (kv.B,))
+    _check(lib.s3r_sparse_draft_round(
+        kv.ref(), _dev(bounds, "bounds", kv.dtype, (n_phys, kv.Hkv, 2, kv.D)), rf,
+        _dev(q, "q", kv.dtype, (kv.B, kv.num_q_heads, kv.D)), int(budget_tokens), int(gamma),
+        float(scale), _dev(selected, "selected", torch.int32, (kv.B, kv.Hkv, k)),
+        _dev(num_selected, "num_selected", torch.int32, (kv.B,)), _OUT_DTYPES[out.dtype],
+        _dev(out, "out", None, (kv.B, kv.num_q_heads, kv.D)), ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), _stream(stream)), "s3r_sparse_draft_round")
     return out, selected, num_selected
 
 

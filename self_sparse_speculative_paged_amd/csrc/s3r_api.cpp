@@ -271,10 +271,17 @@ size_t s3r_sparse_draft_step_workspace(const s3r_paged_kv* kv, int32_t budget_to
   return plan_draft_step(*kv, budget_tokens).workspace_bytes;
 }
 
-s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
-                                 const void* q, int32_t budget_tokens, float softmax_scale,
-                                 int32_t* selected, int32_t* num_selected, s3r_dtype out_dtype,
-                                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One draft step; round_gamma > 0 makes its selection the round's (forced
+// pages kept, reused by the round's later steps).
+s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
+                      const void* q, int32_t budget_tokens, int32_t round_gamma,
+                      float softmax_scale, int32_t* selected, int32_t* num_selected,
+                      s3r_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (s3r_status s = check_attention(kv, q, 1, softmax_scale, out_dtype, out)) return s;
   if (bounds == nullptr || selected == nullptr || num_selected == nullptr) return S3R_ERR_INVALID_ARGUMENT;
   if (budget_tokens < kv->page_size) return S3R_ERR_INVALID_ARGUMENT;
@@ -285,6 +292,7 @@ s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int
   const int32_t k = budget_tokens / kv->page_size;
   s3r::SelectArgs sa = select_args(kv, bounds, q, budget_tokens, softmax_scale, selected,
                                    num_selected, workspace);
+  sa.round_gamma = round_gamma;
   const SingleKernelPlan one = plan_single_kernel(*kv, k);
   if (one.ok) {
     s3r::AttnArgs a = attn_args(kv, one.attn, q, nullptr, k, 1, softmax_scale, out_dtype, out, nullptr);
@@ -297,6 +305,7 @@ s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int
     a.bounds_out = bounds;
     a.refresh_from = refresh_from;
     a.sel_scale = softmax_scale;
+    a.round_gamma = round_gamma;
     return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
   }
   if (plan.fused) {
@@ -310,6 +319,7 @@ s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int
     a.sel_out = selected;
     a.nsel_out = num_selected;
     a.list_offset = plan.list_offset;
+    a.round_gamma = round_gamma;
     return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
   }
   // Unfused: bounds refresh, then select, then attention (stream order makes
@@ -332,6 +342,29 @@ s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int
   const s3r::AttnArgs a = attn_args(kv, plan.attn, q, selected, k, 1, softmax_scale, out_dtype, out,
                                     plan.attn.workspace_bytes ? workspace : nullptr);
   return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+s3r_status s3r_sparse_draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
+                                 const void* q, int32_t budget_tokens, float softmax_scale,
+                                 int32_t* selected, int32_t* num_selected, s3r_dtype out_dtype,
+                                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return draft_step(kv, bounds, refresh_from, q, budget_tokens, 0, softmax_scale, selected,
+                    num_selected, out_dtype, out, workspace, workspace_bytes, stream);
+}
+
+s3r_status s3r_sparse_draft_round(const s3r_paged_kv* kv, void* bounds, const int32_t* refresh_from,
+                                  const void* q, int32_t budget_tokens, int32_t gamma,
+                                  float softmax_scale, int32_t* selected, int32_t* num_selected,
+                                  s3r_dtype out_dtype, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (s3r_status s = check_kv(kv)) return s;
+  if (gamma < 1 || gamma > kMaxGamma || budget_tokens < 2 * kv->page_size) return S3R_ERR_INVALID_ARGUMENT;
+  return draft_step(kv, bounds, refresh_from, q, budget_tokens, gamma, softmax_scale, selected,
+                    num_selected, out_dtype, out, workspace, workspace_bytes, stream);
 }
 
 s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t n_q,

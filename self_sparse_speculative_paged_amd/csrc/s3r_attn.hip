@@ -1,8 +1,8 @@
 // Paged GQA attention for the sparse draft and the dense verify.
 //
 // "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
-// Abstract: the draft attends sparsely, the verify attends to the complete KV
-// history; draft and verify share parameters and therefore one KV cache. Both
+// Abstract: drafting reads part of the KV cache and verifying reads all of it;
+// as drafter and verifier are one model, both read the same cache. Both
 // are softmax(scale * q K^T) V over a token set; they differ only in which
 // pages are read (a selection row vs every page) and in the number of query
 // positions (1 vs gamma + 1, causally masked).
@@ -244,7 +244,8 @@ constexpr int kSelScoreHere = 2;   // score every page here, then top-k
 // taken) skips the bounds reads but still refreshes and copies the ids.
 template <int kD, int kG, int kThreads>
 __device__ __forceinline__ void score_row_to_lds(const AttnArgs& a, int b, int h, int seq_len,
-                                                 int n, bool score, float* sc, int32_t* pt_lds) {
+                                                 int n, bool score, const ForcedPages& fp, float* sc,
+                                                 int32_t* pt_lds) {
   constexpr int kLpp = kD / 8;
   constexpr int kGroups = kThreads / kLpp;  // pages per block-wide step
   constexpr int kIter = 8;                  // pages per page group per batch
@@ -264,7 +265,7 @@ __device__ __forceinline__ void score_row_to_lds(const AttnArgs& a, int b, int h
                                  min(kPage, seq_len - kPage * j), c, lo, hi);
     if (score) {
       const float s = qs.score(lo, hi, a.sel_scale);
-      if (c == 0) sc[j] = s;
+      if (c == 0) sc[j] = j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : s;
     }
     if (c == 1) pt_lds[j] = phys;
   }
@@ -300,7 +301,7 @@ __device__ __forceinline__ void score_row_to_lds(const AttnArgs& a, int b, int h
       const int j = base + grp + kGroups * i;
       if (score) {
         const float s = qs.score(lo[i], hi[i], a.sel_scale);
-        if (c == 0) sc[j] = s;
+        if (c == 0) sc[j] = j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : s;
       }
       if (c == 1) pt_lds[j] = cur[i];
     }
@@ -348,23 +349,23 @@ void attn_bf16_kernel(AttnArgs a) {
     int32_t* list = reinterpret_cast<int32_t*>(lds_bytes + a.list_offset);
     const int k = a.ksel;
     const float* scores = a.scores + (size_t)bh * a.max_pages;
+    const ForcedPages fp = round_forced_pages(seq_len, a.round_gamma, kPage, a.max_pages);
+    int fut0, nfut;
+    future_forced(fp.f0, fp.f1, n_pages, fut0, nfut);
     if constexpr (kSelect == kSelScoreHere) {
       int32_t* pt_lds = reinterpret_cast<int32_t*>(lds_bytes + a.pt_offset);
       float* sc = reinterpret_cast<float*>(lds_bytes);
-      score_row_to_lds<kD, kG, 64 * kW>(a, b, h, seq_len, n_pages, k < n_pages, sc, pt_lds);
+      score_row_to_lds<kD, kG, 64 * kW>(a, b, h, seq_len, n_pages, k - nfut < n_pages, fp, sc, pt_lds);
       __syncthreads();
       scores = sc;
       pt_row = pt_lds;
     }
-    if (k < n_pages)
-      block_topk<64 * kW, kFusedTopkKeys>(scores, n_pages, k, sh, list);
-    else
-      for (int t = threadIdx.x; t < k; t += 64 * kW) list[t] = t < n_pages ? t : -1;
+    select_pages<64 * kW, kFusedTopkKeys>(scores, n_pages, k, fut0, nfut, sh, list);
     __syncthreads();
     if (group == 0) {
       int32_t* out = a.sel_out + (size_t)bh * k;
       for (int t = threadIdx.x; t < k; t += 64 * kW) out[t] = list[t];
-      if (h == 0 && threadIdx.x == 0) a.nsel_out[b] = min(k, n_pages);
+      if (h == 0 && threadIdx.x == 0) a.nsel_out[b] = min(k - nfut, n_pages) + nfut;
     }
     if (g0 >= n_items && a.n_groups > 1) return;  // uniform: the whole group
     sel_row = list;

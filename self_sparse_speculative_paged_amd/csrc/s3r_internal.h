@@ -26,6 +26,26 @@ struct SplitPlan {
 
 SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items);
 
+// Once-per-round selection: logical pages [f0, f1] hold the positions of the
+// round's gamma draft queries, seq_len - 1 .. seq_len + gamma - 2 (seq_len at
+// draft step 0), clipped below at 0 and to the table width; empty (f1 < f0)
+// when gamma == 0 or no such position exists. These pages are always selected.
+struct ForcedPages {
+  int32_t f0, f1;
+};
+
+__host__ __device__ inline ForcedPages round_forced_pages(int32_t seq_len, int32_t gamma,
+                                                          int32_t page_size, int32_t max_pages) {
+  ForcedPages f{0, -1};
+  if (gamma <= 0) return f;
+  const int32_t lo = seq_len > 1 ? seq_len - 1 : 0;
+  const int32_t hi = seq_len + gamma - 2;
+  if (hi < lo) return f;
+  f.f0 = lo / page_size;
+  f.f1 = hi / page_size < max_pages - 1 ? hi / page_size : max_pages - 1;
+  return f;
+}
+
 struct AttnArgs {
   const void* k_pool;
   const void* v_pool;
@@ -52,6 +72,7 @@ struct AttnArgs {
   // bounds_out) with sel_scale, keeping its page-table row in LDS at pt_offset.
   int32_t score_here;
   int32_t pt_offset;
+  int32_t round_gamma;      // > 0: once-per-round selection with forced pages
   const void* bounds;
   void* bounds_out;
   const int32_t* refresh_from;
@@ -84,6 +105,7 @@ struct SelectArgs {
   int32_t* num_selected;
   int32_t B, Hq, Hkv, G, D, max_pages, k;
   float scale;
+  int32_t round_gamma;  // > 0: once-per-round selection with forced pages
 };
 
 hipError_t launch_select(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t stream);

@@ -1,8 +1,8 @@
 // Exact speculative sampling of one S3R round.
 //
 // "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
-// Abstract: the response is produced by full-attention verification and exact
-// speculative sampling, so response groups follow the dense policy. The rule is
+// Abstract: a dense check plus speculative sampling leaves the drafted output
+// distributed exactly as the dense policy's. The rule is
 // that of the speculative decoding / speculative sampling works the S3R
 // reference list cites: with p_i = softmax(target_i / T), q_i =
 // softmax(draft_i / T), accept draft x_i iff u_i < p_i(x_i) / q_i(x_i); at the

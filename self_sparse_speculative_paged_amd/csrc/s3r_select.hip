@@ -1,7 +1,8 @@
 // Page key bounds and query-aware top-k page selection for the sparse draft.
 //
 // "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
-// Abstract: drafting uses sparse attention to cut KV-cache reads. The pages do
+// Abstract: the drafter attends to a subset of the KV cache, which is what makes
+// a draft step cheaper than a dense decode step. The pages do
 // not fix the sparse rule; this library uses a query-aware page rule after the
 // Quest work its reference list cites:
 //   bounds:  kmin/kmax[j][d] = elementwise min/max of the keys of page j;
@@ -128,7 +129,13 @@ void score_kernel(SelectArgs a) {
   int rf = 0x7fffffff;
   if constexpr (sizeof(T) == 2)
     if (a.refresh_from) rf = max(a.refresh_from[b], 0) / kPage;
-  const bool score = a.k < n;  // otherwise every page is taken: the top-k pass writes 0..n-1
+  // A once-per-round selection always keeps its forced pages: they score +inf,
+  // and those not yet in the sequence take selection slots of their own.
+  const ForcedPages fp = round_forced_pages(seq_len, a.round_gamma, kPage, a.max_pages);
+  int fut0, nfut;
+  future_forced(fp.f0, fp.f1, n, fut0, nfut);
+  auto stored = [&](int j, float s) { return j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : s; };
+  const bool score = a.k - nfut < n;  // otherwise every page is taken: the top-k pass writes 0..n-1
   if (!score && (rf >= n || start + kSelectPagesPerBlock <= rf)) return;
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
   float* scores = a.scores + (size_t)bh * a.max_pages;
@@ -162,7 +169,7 @@ void score_kernel(SelectArgs a) {
         const int j = start + grp + kGroups * i;
         if (phys[i] < 0 || j >= rf) continue;  // uniform within the page group
         const float sc = qs.score(kmin[i], kmax[i], a.scale);
-        if (c == 0) scores[j] = sc;
+        if (c == 0) scores[j] = stored(j, sc);
       }
     }
     // Pages from the refresh point on (normally just the tail page): bounds
@@ -178,7 +185,7 @@ void score_kernel(SelectArgs a) {
                                      min(kPage, seq_len - kPage * j), c, lo, hi);
         if (score) {
           const float sc = qs.score(lo, hi, a.scale);
-          if (c == 0) scores[j] = sc;
+          if (c == 0) scores[j] = stored(j, sc);
         }
       }
     }
@@ -215,7 +222,7 @@ void score_kernel(SelectArgs a) {
         }
         best = fmaxf(best, group_sum<kLpp>(acc));
       }
-      if (c == 0) scores[start + grp + kGroups * i] = best * a.scale;
+      if (c == 0) scores[start + grp + kGroups * i] = stored(start + grp + kGroups * i, best * a.scale);
     }
   }
 }
@@ -223,23 +230,21 @@ void score_kernel(SelectArgs a) {
 constexpr int kTopkThreads = 1024;
 
 // One block per (sequence, kv head): the k best pages of its scores, ascending,
-// -1 padded; every page when k >= n.
+// -1 padded; every page when k >= n. A once-per-round selection appends its
+// forced pages that do not exist yet (the others score +inf).
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   __shared__ TopkShared<kTopkThreads> sh;
-  const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh % a.Hkv;
   const int seq_len = a.seq_lens[b];
   const int n = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
+  const ForcedPages fp = round_forced_pages(seq_len, a.round_gamma, kPage, a.max_pages);
+  int fut0, nfut;
+  future_forced(fp.f0, fp.f1, n, fut0, nfut);
   const int k = a.k;
-  int32_t* out = a.selected + (size_t)bh * k;
-  if (h == 0 && tid == 0) a.num_selected[b] = min(k, n);
-  if (k >= n) {
-    for (int t = tid; t < k; t += kTopkThreads) out[t] = t < n ? t : -1;
-    return;
-  }
-  block_topk<kTopkThreads, kMaxSelectPages / kTopkThreads>(a.scores + (size_t)bh * a.max_pages, n,
-                                                          k, sh, out);
+  if (h == 0 && threadIdx.x == 0) a.num_selected[b] = min(k - nfut, n) + nfut;
+  select_pages<kTopkThreads, kMaxSelectPages / kTopkThreads>(a.scores + (size_t)bh * a.max_pages, n, k,
+                                                             fut0, nfut, sh, a.selected + (size_t)bh * k);
 }
 
 template <typename T, int kD>

@@ -180,4 +180,28 @@ __device__ void block_topk(const float* scores, int n, int k, TopkShared<kThread
   }
 }
 
+// The selection list of one (sequence, kv head): the kk = k - nfut best of
+// scores[0..n) (every page if kk >= n), ascending, then the nfut forced pages
+// fut0 .. fut0 + nfut - 1 (>= n: they do not exist yet), then -1 padding.
+// Forced pages below n are expected to carry +inf scores.
+template <int kThreads, int kR>
+__device__ void select_pages(const float* scores, int n, int k, int fut0, int nfut,
+                             TopkShared<kThreads>& sh, int32_t* list) {
+  const int kk = k - nfut;
+  if (kk > 0 && kk < n) block_topk<kThreads, kR>(scores, n, kk, sh, list);
+  const int cnt = kk < n ? (kk > 0 ? kk : 0) : n;
+  for (int t = threadIdx.x; t < k; t += kThreads) {
+    if (t >= cnt)
+      list[t] = t - cnt < nfut ? fut0 + (t - cnt) : -1;
+    else if (kk >= n)
+      list[t] = t;
+  }
+}
+
+// Forced pages at or beyond the n existing ones: (first, count).
+__device__ __forceinline__ void future_forced(int f0, int f1, int n, int& fut0, int& nfut) {
+  fut0 = f0 > n ? f0 : n;
+  nfut = f1 >= fut0 ? f1 - fut0 + 1 : 0;
+}
+
 }  // namespace s3r

@@ -63,6 +63,7 @@ def test_invalid_kv_rejected_everywhere(bad, code):
     assert lib.s3r_attn_workspace(kv, 5, 8) == 0
     assert lib.s3r_page_select_workspace(kv, 64) == 0
     assert lib.s3r_sparse_draft_step(kv, v, None, v, 64, 0.1, v, v, 0, v, v, 1 << 30, None) == code
+    assert lib.s3r_sparse_draft_round(kv, v, None, v, 64, 4, 0.1, v, v, 0, v, v, 1 << 30, None) == code
     assert lib.s3r_sparse_draft_step_workspace(kv, 64) == 0
 
 
@@ -111,6 +112,12 @@ def test_invalid_call_arguments():
     dneed = lib.s3r_sparse_draft_step_workspace(kv, 64)
     assert dneed > 0  # the page scores
     assert d(kv, v, None, v, 64, 0.1, v, v, 0, v, v, dneed - 1, None) == 3
+    r = lib.s3r_sparse_draft_round
+    assert r(kv, v, None, v, 64, 0, 0.1, v, v, 0, v, v, big, None) == 1      # gamma < 1
+    assert r(kv, v, None, v, 64, 17, 0.1, v, v, 0, v, v, big, None) == 1     # gamma > 16
+    assert r(kv, v, None, v, 31, 4, 0.1, v, v, 0, v, v, big, None) == 1      # budget < 2 pages
+    assert r(kv, None, None, v, 64, 4, 0.1, v, v, 0, v, v, big, None) == 1   # bounds
+    assert r(kv, v, None, v, 64, 4, 0.1, v, v, 0, v, v, dneed - 1, None) == 3
 
 
 def test_split_plan_workspace_scales_with_hint():

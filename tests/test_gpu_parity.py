@@ -332,3 +332,59 @@ def test_fused_draft_step_equals_separate_calls(kv, D, G, Hkv, budget, ctx):
         ref = oracle.sparse_draft_attn(f64(q), f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table),
                                        L, i32(sel_b), scale)
         _check_attn(out_b, ref, kv)
+
+
+def _check_round_pages(sel, nsel, rsel, rn, rsc, L, gamma, k, max_pages, tie=1e-4):
+    """Forced pages exactly; the scored rest within the tie window of the oracle's."""
+    assert np.array_equal(nsel, rn), (nsel, rn)
+    for b in range(sel.shape[0]):
+        forced = oracle.round_forced_pages(int(L[b]), gamma, 16, max_pages)
+        for h in range(sel.shape[1]):
+            g = [int(x) for x in sel[b, h] if x >= 0]
+            r = [int(x) for x in rsel[b, h] if x >= 0]
+            assert g == sorted(g) and len(g) == len(r), (b, h, g, r)
+            assert set(forced) <= set(g), (b, h, forced, g)
+            if g == r:
+                continue
+            sc = rsc[(b, h)]
+            kth = sorted(sc.values(), reverse=True)[k - len(forced) - 1]
+            for j in set(g) ^ set(r):
+                assert j in sc and abs(sc[j] - kth) <= tie, (b, h, j, kth)
+
+
+ROUND_CASES = [
+    # kv, D, G, Hkv, budget, gamma, ctx
+    ("bf16", 128, 4, 8, 512, 6, tuple(60 + 97 * i for i in range(32))),  # one kernel
+    ("bf16", 128, 4, 2, 64, 4, (700, 300, 47, 31)),   # two kernels; rounds that open a page
+    ("bf16", 64, 2, 2, 48, 16, (333, 15, 32)),        # gamma 16, short sequences
+    ("f32", 64, 2, 2, 64, 3, (512, 300, 64)),         # fp32: the separate kernels
+    ("bf16", 128, 4, 2, 64, 2, (9000, 200)),          # too many pages for the fused top-k
+]
+
+
+@pytest.mark.parametrize("kv,D,G,Hkv,budget,gamma,ctx", ROUND_CASES)
+def test_round_selection_then_reuse(kv, D, G, Hkv, budget, gamma, ctx):
+    wl = _make(_cfg(kv, D, G, Hkv, gamma=gamma, budget=budget), list(ctx), seed=41)
+    scale = 1.0 / np.sqrt(D)
+    bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(_kv(wl, gamma), bounds)  # stale tail pages until refreshed
+    first = (wl.seq_lens[0] - 1).contiguous()
+    out0, sel, nsel = s3r.sparse_draft_round(_kv(wl, 0), bounds, wl.draft_q(0), budget, gamma,
+                                             scale, refresh_from=first)
+    torch.cuda.synchronize()
+    L0 = i32(wl.seq_lens[0])
+    pt = i32(wl.page_table)
+    rb = oracle.page_bounds(f64(wl.k_pool), pt, L0)
+    used = ~np.isnan(rb[:, 0, 0, 0])
+    assert np.array_equal(f64(bounds)[used], rb[used])
+    rsel, rn, rsc = oracle.page_select_round(rb, f64(wl.draft_q(0)), pt, L0, budget, gamma, scale)
+    _check_round_pages(i32(sel), i32(nsel), rsel, rn, rsc, L0, gamma, budget // 16, pt.shape[1])
+    K, V = f64(wl.k_pool), f64(wl.v_pool)
+    ref = oracle.sparse_draft_attn(f64(wl.draft_q(0)), K, V, pt, L0, i32(sel), scale)
+    _check_attn(out0, ref, kv)
+    for j in range(1, gamma):  # the round's later steps reuse the selection
+        out = s3r.sparse_draft_attn(_kv(wl, j), wl.draft_q(j), sel, scale)
+        torch.cuda.synchronize()
+        ref = oracle.sparse_draft_attn(f64(wl.draft_q(j)), K, V, pt, i32(wl.seq_lens[j]), i32(sel),
+                                       scale)
+        _check_attn(out, ref, kv)
