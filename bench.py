@@ -46,8 +46,10 @@ def parse():
     return p.parse_args()
 
 
-def step_bytes(cfg, ctx):
-    """Algorithmic HBM bytes of one round, summed over sequences."""
+def step_bytes(cfg, ctx, select_once=False):
+    """Algorithmic HBM bytes of one round, summed over sequences. With
+    select_once the bounds are read (and the tail page refreshed) at draft
+    step 0 only; the later steps reuse that selection."""
     P, D, Hkv, Hq, gamma, V = (cfg[k] for k in ("P", "D", "Hkv", "Hq", "gamma", "V"))
     esz = 2 if cfg["kv_dtype"] == "bf16" else 4
     kv_tok = 2 * Hkv * D * esz                  # K + V of one token, all kv heads
@@ -57,9 +59,10 @@ def step_bytes(cfg, ctx):
     for L in ctx:
         for j in range(gamma):
             n = -(-(L + j) // P)
-            parts["select"] += n * bound_page
+            if j == 0 or not select_once:
+                parts["select"] += n * bound_page
+                parts["bounds"] += P * Hkv * D * esz + bound_page   # tail page read + write
             parts["draft"] += min(k, n) * P * kv_tok
-            parts["bounds"] += P * Hkv * D * esz + bound_page   # tail page read + write
             parts["q_out"] += 2 * Hq * D * esz
         parts["verify"] += (L + gamma) * kv_tok
         parts["q_out"] += 2 * (gamma + 1) * Hq * D * esz
@@ -130,6 +133,21 @@ def main():
         verify()
         sample(offset)
 
+    # Variant: select once per round (forced tail pages), reuse for steps 1..gamma-1.
+    sel_r = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    nsel_r = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def one_round_select_once(offset=0):
+        kv.set_seq_lens(wl.seq_lens[0])
+        s3r.sparse_draft_round(kv, bounds, q_draft[0], budget, gamma, scale,
+                               refresh_from=first_pos[0], selected=sel_r, num_selected=nsel_r,
+                               out=d_out[0], workspace=ws_step)
+        for j in range(1, gamma):
+            kv.set_seq_lens(wl.seq_lens[j])
+            s3r.sparse_draft_attn(kv, q_draft[j], sel_r, scale, out=d_out[j], workspace=ws_d)
+        verify()
+        sample(offset)
+
     # eager warm-up, and the accepted-length statistics over several Philox offsets
     for w in range(max(1, args.warmup)):
         one_round(w)
@@ -141,30 +159,36 @@ def main():
     acc = torch.stack(acc).float()
     mean_committed = float((acc + 1).sum(dim=1).mean())  # tokens committed per round, all sequences
 
-    runner = one_round
-    if not args.no_graph:
+    def make_runner(fn):
+        if args.no_graph:
+            return fn
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            one_round(0)
+            fn(0)
         torch.cuda.current_stream().wait_stream(s)
         with torch.cuda.graph(g):
-            one_round(0)
-        runner = g.replay
+            fn(0)
+        graphs.append(g)
+        return g.replay
+
+    def time_runner(runner):
         for _ in range(max(1, args.warmup)):
             runner()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            runner()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
 
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        runner()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    graphs = []
+    ms = time_runner(make_runner(one_round))
+    ms_once = time_runner(make_runner(one_round_select_once))
 
     # Per-launch timing of each entry point (eager, events on the launch stream).
     def time_call(fn, reps):
@@ -196,6 +220,7 @@ def main():
 
     parts = step_bytes(cfg, ctx)
     total_bytes = sum(parts.values())
+    parts_once = step_bytes(cfg, ctx, select_once=True)
     gbs = total_bytes / (ms * 1e-3) / 1e9
     verify_gbs = parts["verify"] / (t_verify * 1e-6) / 1e9
     per_step_draft = parts["draft"] / gamma
@@ -231,6 +256,12 @@ def main():
         "launch_us": {"page_bounds_update": round(t_bounds, 2), "page_select": round(t_select, 2),
                       "sparse_draft_attn": round(t_draft, 2), "sparse_draft_step": round(t_step, 2),
                       "dense_verify_attn": round(t_verify, 2), "spec_sample": round(t_sample, 2)},
+        "select_once": {
+            "ms_per_step": round(ms_once, 4),
+            "value": round(sum(parts_once.values()) / (ms_once * 1e-3) / 1e9, 1),
+            "accepted_tokens_per_s": round(mean_committed / (ms_once * 1e-3), 1),
+            "step_bytes": int(sum(parts_once.values())),
+        },
         "roofline": {"kernel": "dense_verify_attn (attn_bf16_kernel + split combine)",
                      "bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4),

@@ -119,9 +119,31 @@ s3r::SelectArgs select_args(const s3r_paged_kv* kv, const void* bounds, const vo
   return a;
 }
 
+// Eight waves per (sequence, kv head), the selection split evenly over them:
+// the draft's plan whenever its top-k runs inside the attention workgroup.
+s3r::SplitPlan eight_wave_plan(const s3r_paged_kv& kv, int32_t k) {
+  constexpr int kWaves = 8;
+  s3r::SplitPlan a{};
+  const int32_t G = kv.num_q_heads / kv.num_kv_heads;
+  a.rows = G;
+  a.row_blocks = 1;
+  int32_t pps = (k + kWaves - 1) / kWaves;
+  pps = pps < 2 ? 2 : (pps + 1) & ~1;
+  a.pages_per_split = pps;
+  a.n_splits = (k + pps - 1) / pps;
+  a.waves_per_group = kWaves;
+  a.n_groups = 1;
+  const size_t table = sizeof(int) * 4 * (size_t)((pps + 1) / 2);
+  const size_t partial = sizeof(float) * (size_t)G * (kv.head_dim + 2);
+  a.lds_region_bytes = (int32_t)(((table > partial ? table : partial) + 15) & ~(size_t)15);
+  a.workspace_bytes = 0;
+  return a;
+}
+
 // The fused draft step keeps the selection list in LDS after the per-wave
 // regions; it needs bf16 KV, at most 64 KB of LDS and a page table short
-// enough for its in-register top-k.
+// enough for its in-register top-k. A selection that fits one workgroup runs
+// on eight waves, so the top-k has 512 threads.
 struct DraftStepPlan {
   s3r::SplitPlan attn;
   size_t select_ws;
@@ -134,11 +156,14 @@ DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
   DraftStepPlan p{};
   const int32_t k = budget_tokens / kv.page_size;
   p.attn = s3r::plan_attention(kv, 1, k);
+  if (kv.kv_dtype == S3R_BF16 && p.attn.row_blocks == 1 && p.attn.waves_per_group < 8)
+    p.attn = eight_wave_plan(kv, k);
   p.select_ws = s3r::select_workspace_bytes(kv.num_seqs, kv.num_kv_heads, kv.max_pages_per_seq);
-  const size_t regions = (size_t)p.attn.lds_region_bytes * p.attn.waves_per_group;
+  const int32_t w = p.attn.waves_per_group;
+  const size_t regions = (size_t)p.attn.lds_region_bytes * w;
   const size_t list_offset = (regions + 15) & ~(size_t)15;
   p.list_offset = (int32_t)list_offset;
-  p.fused = kv.kv_dtype == S3R_BF16 && kv.max_pages_per_seq <= s3r::kFusedTopkKeys * 64 * p.attn.waves_per_group &&
+  p.fused = kv.kv_dtype == S3R_BF16 && kv.max_pages_per_seq <= s3r::fused_topk_keys(w) * 64 * w &&
             list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
   p.workspace_bytes = p.fused ? p.select_ws + p.attn.workspace_bytes
                               : (p.select_ws > p.attn.workspace_bytes ? p.select_ws : p.attn.workspace_bytes);
@@ -174,21 +199,9 @@ SingleKernelPlan plan_single_kernel(const s3r_paged_kv& kv, int32_t k) {
   SingleKernelPlan p{};
   const int32_t G = kv.num_q_heads / kv.num_kv_heads;
   if (kv.kv_dtype != S3R_BF16 || (G != 1 && G != 2 && G != 4 && G != 8)) return p;
-  if (kv.max_pages_per_seq > s3r::kFusedTopkKeys * 64 * kWaves) return p;
+  if (kv.max_pages_per_seq > s3r::fused_topk_keys(kWaves) * 64 * kWaves) return p;
   if ((int64_t)kv.num_seqs * kv.num_kv_heads < device_cu_count()) return p;
-  s3r::SplitPlan& a = p.attn;
-  a.rows = G;
-  a.row_blocks = 1;
-  int32_t pps = (k + kWaves - 1) / kWaves;
-  pps = pps < 2 ? 2 : (pps + 1) & ~1;
-  a.pages_per_split = pps;
-  a.n_splits = (k + pps - 1) / pps;
-  a.waves_per_group = kWaves;
-  a.n_groups = 1;
-  const size_t table = sizeof(int) * 4 * (size_t)((pps + 1) / 2);
-  const size_t partial = sizeof(float) * (size_t)G * (kv.head_dim + 2);
-  a.lds_region_bytes = (int32_t)(((table > partial ? table : partial) + 15) & ~(size_t)15);
-  a.workspace_bytes = 0;
+  const s3r::SplitPlan& a = p.attn = eight_wave_plan(kv, k);
   const size_t row = sizeof(int32_t) * (size_t)kv.max_pages_per_seq;
   size_t front = (size_t)a.lds_region_bytes * kWaves;
   if (front < row) front = row;  // the scores alias the wave regions
@@ -236,9 +249,10 @@ s3r_status s3r_page_bounds_update(const s3r_paged_kv* kv, void* bounds, const in
   a.Hkv = kv->num_kv_heads;
   a.D = kv->head_dim;
   a.max_pages = kv->max_pages_per_seq;
-  a.pages_y = first_pos ? (max_pages_touched < kv->max_pages_per_seq ? max_pages_touched
-                                                                     : kv->max_pages_per_seq)
-                        : kv->max_pages_per_seq;
+  a.span = first_pos ? (max_pages_touched < kv->max_pages_per_seq ? max_pages_touched
+                                                                  : kv->max_pages_per_seq)
+                     : kv->max_pages_per_seq;
+  a.pages_y = a.span;
   return from_hip(s3r::launch_bounds(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -335,7 +349,8 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
     ba.Hkv = kv->num_kv_heads;
     ba.D = kv->head_dim;
     ba.max_pages = kv->max_pages_per_seq;
-    ba.pages_y = kv->max_pages_per_seq;
+    ba.span = kv->max_pages_per_seq;  // every page from refresh_from / P to the tail,
+    ba.pages_y = 2;                   // normally just the tail page
     if (hipError_t e = s3r::launch_bounds(ba, kv->kv_dtype, st)) return from_hip(e);
   }
   if (hipError_t e = s3r::launch_select(sa, kv->kv_dtype, st)) return from_hip(e);

@@ -360,7 +360,7 @@ void attn_bf16_kernel(AttnArgs a) {
       scores = sc;
       pt_row = pt_lds;
     }
-    select_pages<64 * kW, kFusedTopkKeys>(scores, n_pages, k, fut0, nfut, sh, list);
+    select_pages<64 * kW, fused_topk_keys(kW)>(scores, n_pages, k, fut0, nfut, sh, list);
     __syncthreads();
     if (group == 0) {
       int32_t* out = a.sel_out + (size_t)bh * k;

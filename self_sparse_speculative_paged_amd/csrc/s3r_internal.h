@@ -87,7 +87,8 @@ struct BoundsArgs {
   const int32_t* seq_lens;
   const int32_t* first_pos;  // nullptr = all pages
   void* bounds;
-  int32_t B, Hkv, D, max_pages, pages_y;
+  int32_t B, Hkv, D, max_pages, pages_y;  // grid rows: pages handled together per (seq, head)
+  int32_t span;                           // pages from first_pos / P the call covers
 };
 
 hipError_t launch_bounds(const BoundsArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
@@ -114,10 +115,10 @@ hipError_t launch_select(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t st
 hipError_t launch_scores(const SelectArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
 size_t select_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_pages);
 int32_t select_max_pages_supported();
-// Page keys per thread of the fused draft step's in-register top-k: a kW-wave
-// workgroup ranks at most kFusedTopkKeys * 64 * kW pages per sequence; longer
-// page tables take the separate select kernel.
-constexpr int kFusedTopkKeys = 8;
+// Page keys per thread of the fused draft step's in-register top-k: a W-wave
+// workgroup ranks at most fused_topk_keys(W) * 64 * W pages per sequence
+// (8192 at W = 8); longer page tables take the separate select kernel.
+constexpr int fused_topk_keys(int waves) { return waves >= 8 ? 16 : 8; }
 
 struct SampleArgs {
   const float* draft_logits;

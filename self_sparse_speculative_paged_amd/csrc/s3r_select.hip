@@ -39,72 +39,74 @@ __global__ __launch_bounds__(64) void bounds_kernel(BoundsArgs a) {
   const int n = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   int first = 0;
   if (a.first_pos) first = max(a.first_pos[b], 0) / kPage;
-  const int j = first + blockIdx.y;
-  if (j >= n) return;
-  const int valid = min(kPage, seq_len - kPage * j);
-  const int phys = a.page_table[(size_t)b * a.max_pages + j];
-  const int c = lane % kLpr, rg = lane / kLpr;
-  const T* kbase = static_cast<const T*>(a.k_pool) + (((size_t)phys * a.Hkv + h) * kPage) * kD + 8 * c;
+  // Pages first .. first + span - 1 (clipped to the sequence), gridDim.y apart.
+  const int j_end = (int)min((long)n, (long)first + a.span);
+  for (int j = first + blockIdx.y; j < j_end; j += gridDim.y) {
+    const int valid = min(kPage, seq_len - kPage * j);
+    const int phys = a.page_table[(size_t)b * a.max_pages + j];
+    const int c = lane % kLpr, rg = lane / kLpr;
+    const T* kbase = static_cast<const T*>(a.k_pool) + (((size_t)phys * a.Hkv + h) * kPage) * kD + 8 * c;
 
-  float mn[8], mx[8];
+    float mn[8], mx[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mn[e] = __builtin_huge_valf();
-    mx[e] = -__builtin_huge_valf();
-  }
-  // Every row this lane covers is loaded before any is folded (one round trip).
-  constexpr int kRows = kPage / kRg;
-  float v[kRows][8];
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = __builtin_huge_valf();
+      mx[e] = -__builtin_huge_valf();
+    }
+    // Every row this lane covers is loaded before any is folded (one round trip).
+    constexpr int kRows = kPage / kRg;
+    float v[kRows][8];
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    const int t = rg + kRg * i;
-    const T* row = kbase + (size_t)(t < valid ? t : 0) * kD;
-    if constexpr (sizeof(T) == 2) {
-      const uint4 raw = load_nt16<uint4>(row);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int i = 0; i < kRows; ++i) {
+      const int t = rg + kRg * i;
+      const T* row = kbase + (size_t)(t < valid ? t : 0) * kD;
+      if constexpr (sizeof(T) == 2) {
+        const uint4 raw = load_nt16<uint4>(row);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[i][2 * e] = __uint_as_float(w[e] << 16);
-        v[i][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
-    } else {
-      const f32x4 lo4 = load_nt16<f32x4>(row);
-      const f32x4 hi4 = load_nt16<f32x4>(row + 4);
+        for (int e = 0; e < 4; ++e) {
+          v[i][2 * e] = __uint_as_float(w[e] << 16);
+          v[i][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 lo4 = load_nt16<f32x4>(row);
+        const f32x4 hi4 = load_nt16<f32x4>(row + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[i][e] = lo4[e];
-        v[i][4 + e] = hi4[e];
+        for (int e = 0; e < 4; ++e) {
+          v[i][e] = lo4[e];
+          v[i][4 + e] = hi4[e];
+        }
       }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    if (rg + kRg * i < valid) {
+    for (int i = 0; i < kRows; ++i) {
+      if (rg + kRg * i < valid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mn[e] = fminf(mn[e], v[i][e]);
+          mx[e] = fmaxf(mx[e], v[i][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int x = kLpr; x < 64; x <<= 1) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        mn[e] = fminf(mn[e], v[i][e]);
-        mx[e] = fmaxf(mx[e], v[i][e]);
+        mn[e] = fminf(mn[e], __shfl_xor(mn[e], x, 64));
+        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], x, 64));
       }
     }
-  }
+    if (rg == 0) {
+      T* out = static_cast<T*>(a.bounds) + (((size_t)phys * a.Hkv + h) * 2) * kD + 8 * c;
 #pragma unroll
-  for (int x = kLpr; x < 64; x <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mn[e] = fminf(mn[e], __shfl_xor(mn[e], x, 64));
-      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], x, 64));
-    }
-  }
-  if (rg == 0) {
-    T* out = static_cast<T*>(a.bounds) + (((size_t)phys * a.Hkv + h) * 2) * kD + 8 * c;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (sizeof(T) == 2) {
-        reinterpret_cast<uint16_t*>(out)[e] = f32_to_bf16_bits(mn[e]);
-        reinterpret_cast<uint16_t*>(out)[kD + e] = f32_to_bf16_bits(mx[e]);
-      } else {
-        reinterpret_cast<float*>(out)[e] = mn[e];
-        reinterpret_cast<float*>(out)[kD + e] = mx[e];
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (sizeof(T) == 2) {
+          reinterpret_cast<uint16_t*>(out)[e] = f32_to_bf16_bits(mn[e]);
+          reinterpret_cast<uint16_t*>(out)[kD + e] = f32_to_bf16_bits(mx[e]);
+        } else {
+          reinterpret_cast<float*>(out)[e] = mn[e];
+          reinterpret_cast<float*>(out)[kD + e] = mx[e];
+        }
       }
     }
   }

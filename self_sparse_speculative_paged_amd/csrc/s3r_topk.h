@@ -38,7 +38,7 @@ struct TopkShared {
 // Writes the k best of scores[0..n) (requires k < n <= kR * kThreads, n < 65536)
 // to out[0..k) in ascending page order. Every thread of the block calls it.
 template <int kThreads, int kR>
-__device__ void block_topk(const float* scores, int n, int k, TopkShared<kThreads>& sh,
+__device__ __forceinline__ void block_topk(const float* scores, int n, int k, TopkShared<kThreads>& sh,
                            int32_t* out) {
   constexpr int kWaves = kThreads / 64;
   static_assert(kThreads % 64 == 0 && kWaves <= 16, "1 to 16 waves");
@@ -185,7 +185,7 @@ __device__ void block_topk(const float* scores, int n, int k, TopkShared<kThread
 // fut0 .. fut0 + nfut - 1 (>= n: they do not exist yet), then -1 padding.
 // Forced pages below n are expected to carry +inf scores.
 template <int kThreads, int kR>
-__device__ void select_pages(const float* scores, int n, int k, int fut0, int nfut,
+__device__ __forceinline__ void select_pages(const float* scores, int n, int k, int fut0, int nfut,
                              TopkShared<kThreads>& sh, int32_t* list) {
   const int kk = k - nfut;
   if (kk > 0 && kk < n) block_topk<kThreads, kR>(scores, n, kk, sh, list);

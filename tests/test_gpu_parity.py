@@ -288,8 +288,9 @@ FUSED_CASES = [
     ("bf16", 128, 2, 2, 1024, (3000, 100)),    # selection longer than one workgroup's splits
     ("bf16", 64, 8, 1, 48, (333, 15)),
     ("bf16", 128, 4, 2, 4096, (100, 50)),      # budget covers every page
-    ("bf16", 64, 4, 2, 64, (8000, 7990)),      # one wave, eight key chunks per thread
-    ("bf16", 128, 4, 2, 64, (9000, 200)),      # too many pages for the fused top-k
+    ("bf16", 64, 4, 2, 64, (8000, 7990)),      # 4 pages of 500, eight waves
+    ("bf16", 128, 4, 2, 64, (9000, 200)),      # 4 pages of 563
+    ("bf16", 64, 2, 1, 64, (140000, 300)),     # 8750 pages: past the fused top-k
     # 32 sequences x 8 kv heads fill the device: the single-kernel step (scores
     # in LDS); ragged lengths, some short enough that every page is taken
     ("bf16", 128, 4, 8, 512, tuple(60 + 97 * i for i in range(32))),
@@ -358,7 +359,8 @@ ROUND_CASES = [
     ("bf16", 128, 4, 2, 64, 4, (700, 300, 47, 31)),   # two kernels; rounds that open a page
     ("bf16", 64, 2, 2, 48, 16, (333, 15, 32)),        # gamma 16, short sequences
     ("f32", 64, 2, 2, 64, 3, (512, 300, 64)),         # fp32: the separate kernels
-    ("bf16", 128, 4, 2, 64, 2, (9000, 200)),          # too many pages for the fused top-k
+    ("bf16", 128, 4, 2, 64, 2, (9000, 200)),          # 563 pages, two kernels
+    ("bf16", 64, 2, 1, 64, 5, (140000, 300)),         # 8750 pages: past the fused top-k
 ]
 
 
