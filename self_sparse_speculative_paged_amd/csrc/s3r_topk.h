@@ -46,15 +46,20 @@ __device__ __forceinline__ void block_topk(const float* scores, int n, int k, To
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  // Every loop over chunks skips the chunks past n with a uniform branch, so
+  // the work follows n rather than the capacity kR.
+  const int nchunks = (n + kThreads - 1) / kThreads;
   uint32_t key[kR];
 #pragma unroll
   for (int e = 0; e < kR; ++e) {
+    if (e >= nchunks) break;
     const int j = e * kThreads + tid;
     key[e] = j < n ? order_key(scores[j]) : 0u;
   }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int e = 0; e < kR; ++e) {
+    if (e >= nchunks) break;
     if (e * kThreads + tid < n) {
       kmin = min(kmin, key[e]);
       kmax = max(kmax, key[e]);
@@ -89,6 +94,7 @@ __device__ __forceinline__ void block_topk(const float* scores, int n, int k, To
     for (int i = tid; i < kTopkBins; i += kThreads) sh.hist[nxt][i] = 0;
 #pragma unroll
     for (int e = 0; e < kR; ++e) {
+      if (e >= nchunks) break;
       if (e * kThreads + tid < n && (key[e] & mask) == prefix)
         atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
     }
@@ -140,7 +146,8 @@ __device__ __forceinline__ void block_topk(const float* scores, int n, int k, To
   // lanes below in the wave, gives gt(p) and eq(p), the keys above and equal
   // to thr before position p. The key at p, if taken, lands at gt(p) + min(eq(p), krem).
   uint32_t* wc = sh.hist[cur];
-  const int nchunks = (n + kThreads - 1) / kThreads;
+  // (Ballots are convergent: these two loops keep a uniform guard instead of a
+  // break, which would stop them from unrolling.)
 #pragma unroll
   for (int e = 0; e < kR; ++e) {
     if (e < nchunks) {
