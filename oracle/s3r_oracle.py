@@ -55,6 +55,7 @@ __all__ = [
     "philox4x64_10", "uniform",
     "key_row", "value_row", "n_pages",
     "page_bounds", "page_scores", "page_select", "round_forced_pages", "page_select_round",
+    "kv_commit",
     "attend", "sparse_draft_attn", "dense_verify_attn", "decode_streaming",
     "softmax", "icdf", "spec_sample", "draw_draft_tokens",
 ]
@@ -136,6 +137,49 @@ def page_bounds(k_pool, page_table, seq_lens, seqs=None):
                 out[phys, h, 0] = rows.min(axis=0)
                 out[phys, h, 1] = rows.max(axis=0)
     return out
+
+
+def kv_commit(k_pool, v_pool, page_table, k_new, v_new, first_pos, seq_lens, bounds):
+    """Write new K/V rows into their pages, then bring the touched pages' bounds
+    up to date for the committed lengths.
+
+    The step either side of a round: the rows a forward pass produced are
+    appended to the shared cache, and after the accept/reject decision the
+    sequence's length is set back to what was committed. Row i of sequence b
+    (k_new[b, i], v_new[b, i]: [Hkv][D]) goes to position first_pos[b] + i:
+    logical page pos // P, slot pos % P, V transposed inside the page; rows
+    past the page table are dropped. seq_lens[b] is the committed length after
+    the call; it may end inside the rows just written (a rollback: those rows
+    stay in the pool but no longer count). Every logical page from
+    min(first_pos[b], seq_lens[b] - 1) // P through the last page written or
+    the tail page of seq_lens[b] gets its bounds recomputed over its tokens
+    below seq_lens[b] (page_bounds' rule); a page left without valid tokens
+    keeps its old bounds. Other pages are untouched.
+
+    Returns new (k_pool, v_pool, bounds) arrays.
+    """
+    K, V, Bd = k_pool.copy(), v_pool.copy(), bounds.copy()
+    n_phys, hkv, P, D = K.shape
+    B, max_pages = page_table.shape
+    count = k_new.shape[1]
+    for b in range(B):
+        f = int(first_pos[b])
+        for i in range(count):
+            pos = f + i
+            if pos // P >= max_pages:
+                continue
+            phys = page_table[b, pos // P]
+            K[phys, :, pos % P, :] = k_new[b, i]
+            V[phys, :, :, pos % P] = v_new[b, i]
+    fresh = page_bounds(K, page_table, seq_lens)
+    for b in range(B):
+        f, L = int(first_pos[b]), int(seq_lens[b])
+        lo = min(f, max(L - 1, 0)) // P
+        hi = max((f + count - 1) // P if count > 0 else -1, n_pages(L, P) - 1)
+        for j in range(lo, min(hi, max_pages - 1) + 1):
+            if j < n_pages(L, P):
+                Bd[page_table[b, j]] = fresh[page_table[b, j]]
+    return K, V, Bd
 
 
 def page_scores(bounds, q, page_table, seq_lens, scale, b, h, P=16):
