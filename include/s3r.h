@@ -186,6 +186,31 @@ s3r_status s3r_sparse_draft_round(const s3r_paged_kv* kv, void* bounds, const in
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * s3r_kv_commit: the KV step either side of a round. It writes new K/V rows
+ * (what a draft or verify forward pass produced) into their pages and keeps
+ * the page bounds exact for the committed lengths; a length below rows already
+ * written rolls them back. S3R Abstract: drafter and verifier are one model
+ * over one KV cache, so these rows are the ones the sparse draft later ranks.
+ *   kv          seq_lens holds the committed lengths AFTER the call. The call
+ *               writes the pools kv->k_pool and kv->v_pool point at.
+ *   k_new, v_new  [B][count][Hkv][D] kv dtype, 16-byte aligned: row i of
+ *               sequence b goes to position first_pos[b] + i (logical page
+ *               pos / P via page_table, slot pos % P; V transposed inside the
+ *               page). Rows past max_pages_per_seq pages are dropped.
+ *   first_pos   [B] int32, >= 0.
+ *   count       rows per sequence, >= 0 (0: a pure rollback).
+ *   bounds      in/out [num_phys_pages][Hkv][2][D] kv dtype, or NULL for no
+ *               bounds upkeep. Every logical page from
+ *               min(first_pos[b], seq_len - 1) / P through the last written
+ *               page or the tail page of seq_len is recomputed over its tokens
+ *               < seq_len, if it has any; other pages are left alone.
+ * Errors: INVALID_ARGUMENT for count < 0, NULL first_pos, NULL or misaligned
+ * rows when count > 0; otherwise as check of kv. No workspace.
+ */
+s3r_status s3r_kv_commit(const s3r_paged_kv* kv, const void* k_new, const void* v_new,
+                         const int32_t* first_pos, int32_t count, void* bounds, void* stream);
+
+/*
  * s3r_dense_verify_attn: full-attention verification of the draft (S3R
  * Abstract: verifying reads every cached key and value of the sequence).
  * Query i = 0..n_q-1 of sequence b sits at position seq_len - n_q + i and

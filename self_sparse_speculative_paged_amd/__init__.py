@@ -9,7 +9,8 @@ in (pre-allocated, e.g. for timing or graph capture) or are allocated here.
 Entry points (same names as include/s3r.h without the prefix):
   page_bounds_update, page_select, sparse_draft_attn, sparse_draft_step (the
   three fused), sparse_draft_round (a draft step whose selection the round's
-  later steps reuse), dense_verify_attn, spec_sample, and the workspace queries.
+  later steps reuse), kv_commit (write new K/V rows, keep the bounds exact,
+  roll back), dense_verify_attn, spec_sample, and the workspace queries.
 """
 import ctypes
 
@@ -22,7 +23,7 @@ __all__ = [
     "S3RError", "PagedKVCache", "page_bounds_update", "page_select", "sparse_draft_attn",
     "dense_verify_attn", "spec_sample", "page_select_workspace", "attn_workspace",
     "spec_sample_workspace", "version", "sparse_draft_step", "sparse_draft_step_workspace",
-    "sparse_draft_round",
+    "sparse_draft_round", "kv_commit",
 ]
 
 _KV_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
@@ -223,6 +224,22 @@ def sparse_draft_round(kv, bounds, q, budget_tokens, gamma, scale, refresh_from=
         _dev(out, "out", None, (kv.B, kv.num_q_heads, kv.D)), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(stream)), "s3r_sparse_draft_round")
     return out, selected, num_selected
+
+
+def kv_commit(kv, k_new, v_new, first_pos, bounds=None, stream=None):
+    """Write k_new/v_new [B][count][Hkv][D] at positions first_pos[b] + i into the
+    pools of kv and bring the touched pages' bounds up to date for kv's
+    seq_lens (the committed lengths); returns bounds."""
+    lib = _lib.load()
+    B, count = k_new.shape[0], k_new.shape[1]
+    shape = (kv.B, count, kv.Hkv, kv.D)
+    n_phys = kv.k_pool.shape[0]
+    b = None if bounds is None else _dev(bounds, "bounds", kv.dtype, (n_phys, kv.Hkv, 2, kv.D))
+    _check(lib.s3r_kv_commit(
+        kv.ref(), _dev(k_new, "k_new", kv.dtype, shape), _dev(v_new, "v_new", kv.dtype, shape),
+        _dev(first_pos, "first_pos", torch.int32, (kv.B,)), int(count), b, _stream(stream)),
+        "s3r_kv_commit")
+    return bounds
 
 
 def dense_verify_attn(kv, q, scale, out=None, out_dtype=torch.float32, workspace=None,

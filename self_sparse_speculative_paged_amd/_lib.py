@@ -22,6 +22,7 @@ EXPORTS = [
     "s3r_page_bounds_update", "s3r_page_select", "s3r_sparse_draft_attn",
     "s3r_dense_verify_attn", "s3r_spec_sample", "s3r_status_string", "s3r_version",
     "s3r_sparse_draft_step_workspace", "s3r_sparse_draft_step", "s3r_sparse_draft_round",
+    "s3r_kv_commit",
 ]
 
 
@@ -70,6 +71,7 @@ def load():
         "s3r_sparse_draft_step_workspace": (sz, [P, i32]),
         "s3r_sparse_draft_step": (i32, [P, vp, vp, vp, i32, f32, vp, vp, i32, vp, vp, sz, vp]),
         "s3r_sparse_draft_round": (i32, [P, vp, vp, vp, i32, i32, f32, vp, vp, i32, vp, vp, sz, vp]),
+        "s3r_kv_commit": (i32, [P, vp, vp, vp, i32, vp, vp]),
         "s3r_spec_sample": (i32, [i32, i32, i32, vp, vp, vp, f32, u64, u64, vp, vp, vp, sz, vp]),
         "s3r_status_string": (ctypes.c_char_p, [i32]),
         "s3r_version": (i32, []),

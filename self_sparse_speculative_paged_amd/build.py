@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libs3r.so")
-SOURCES = ["s3r_api.cpp", "s3r_attn.hip", "s3r_select.hip", "s3r_sample.hip"]
+SOURCES = ["s3r_api.cpp", "s3r_attn.hip", "s3r_select.hip", "s3r_sample.hip", "s3r_kv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

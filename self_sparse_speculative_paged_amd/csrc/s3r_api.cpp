@@ -382,6 +382,32 @@ s3r_status s3r_sparse_draft_round(const s3r_paged_kv* kv, void* bounds, const in
                     num_selected, out_dtype, out, workspace, workspace_bytes, stream);
 }
 
+s3r_status s3r_kv_commit(const s3r_paged_kv* kv, const void* k_new, const void* v_new,
+                         const int32_t* first_pos, int32_t count, void* bounds, void* stream) {
+  if (s3r_status s = check_kv(kv)) return s;
+  if (first_pos == nullptr || count < 0) return S3R_ERR_INVALID_ARGUMENT;
+  if (count > 0 && (k_new == nullptr || v_new == nullptr)) return S3R_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return S3R_ERR_INVALID_ARGUMENT;  // rows are moved as 16-byte runs
+  s3r::KvCommitArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.first_pos = first_pos;
+  // The struct's pool pointers are const for the read-only calls; this one
+  // writes the caller's pools through them.
+  a.k_pool = const_cast<void*>(kv->k_pool);
+  a.v_pool = const_cast<void*>(kv->v_pool);
+  a.page_table = kv->page_table;
+  a.seq_lens = kv->seq_lens;
+  a.bounds = bounds;
+  a.B = kv->num_seqs;
+  a.Hkv = kv->num_kv_heads;
+  a.D = kv->head_dim;
+  a.max_pages = kv->max_pages_per_seq;
+  a.count = count;
+  return from_hip(s3r::launch_kv_commit(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
 s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t n_q,
                                  float softmax_scale, s3r_dtype out_dtype, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream) {

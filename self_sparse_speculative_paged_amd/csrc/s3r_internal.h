@@ -93,6 +93,20 @@ struct BoundsArgs {
 
 hipError_t launch_bounds(const BoundsArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
 
+struct KvCommitArgs {
+  const void* k_new;      // [B][count][Hkv][D]
+  const void* v_new;      // [B][count][Hkv][D]
+  const int32_t* first_pos;
+  void* k_pool;           // written
+  void* v_pool;           // written
+  const int32_t* page_table;
+  const int32_t* seq_lens;  // committed lengths after the call
+  void* bounds;           // nullptr: no bounds upkeep
+  int32_t B, Hkv, D, max_pages, count;
+};
+
+hipError_t launch_kv_commit(const KvCommitArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
+
 struct SelectArgs {
   const void* bounds;
   void* bounds_out;             // == bounds when refresh_from is set (bf16 only)

@@ -64,6 +64,7 @@ def test_invalid_kv_rejected_everywhere(bad, code):
     assert lib.s3r_page_select_workspace(kv, 64) == 0
     assert lib.s3r_sparse_draft_step(kv, v, None, v, 64, 0.1, v, v, 0, v, v, 1 << 30, None) == code
     assert lib.s3r_sparse_draft_round(kv, v, None, v, 64, 4, 0.1, v, v, 0, v, v, 1 << 30, None) == code
+    assert lib.s3r_kv_commit(kv, v, v, v, 4, v, None) == code
     assert lib.s3r_sparse_draft_step_workspace(kv, 64) == 0
 
 
@@ -112,6 +113,11 @@ def test_invalid_call_arguments():
     dneed = lib.s3r_sparse_draft_step_workspace(kv, 64)
     assert dneed > 0  # the page scores
     assert d(kv, v, None, v, 64, 0.1, v, v, 0, v, v, dneed - 1, None) == 3
+    c = lib.s3r_kv_commit
+    assert c(kv, v, v, None, 4, v, None) == 1                    # first_pos
+    assert c(kv, v, v, v, -1, v, None) == 1                      # count < 0
+    assert c(kv, None, v, v, 4, v, None) == 1                    # rows
+    assert c(kv, ctypes.c_void_p(FAKE + 8), v, v, 4, v, None) == 1   # misaligned rows
     r = lib.s3r_sparse_draft_round
     assert r(kv, v, None, v, 64, 0, 0.1, v, v, 0, v, v, big, None) == 1      # gamma < 1
     assert r(kv, v, None, v, 64, 17, 0.1, v, v, 0, v, v, big, None) == 1     # gamma > 16

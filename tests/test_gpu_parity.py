@@ -390,3 +390,35 @@ def test_round_selection_then_reuse(kv, D, G, Hkv, budget, gamma, ctx):
         ref = oracle.sparse_draft_attn(f64(wl.draft_q(j)), K, V, pt, i32(wl.seq_lens[j]), i32(sel),
                                        scale)
         _check_attn(out, ref, kv)
+
+
+COMMIT_CASES = [
+    # kv, D, Hkv, ctx, count, table slack (gamma), accepted per sequence
+    ("bf16", 128, 2, (40, 17, 64, 100), 7, 8, (6, 0, 2, 7)),
+    ("f32", 64, 2, (15, 16, 200), 3, 4, (2, 2, 0)),
+    ("bf16", 64, 3, (33, 1), 1, 2, (0, 1)),
+    ("bf16", 128, 2, (60,), 8, 2, (4,)),          # rows past the table are dropped
+    ("bf16", 128, 2, (45, 70), 0, 2, (-10, -3)),  # a pure rollback
+]
+
+
+@pytest.mark.parametrize("kv,D,Hkv,ctx,count,slack,accepted", COMMIT_CASES)
+def test_kv_commit_matches_oracle(kv, D, Hkv, ctx, count, slack, accepted):
+    wl = _make(_cfg(kv, D, 2, Hkv, gamma=slack), list(ctx), seed=51)
+    dt = wl.k_pool.dtype
+    bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=dt, device=DEV)
+    s3r.page_bounds_update(_kv(wl, 0), bounds)
+    first = (wl.seq_lens[0] - 1).contiguous()
+    committed = (first + 1 + torch.tensor(accepted, dtype=torch.int32, device=DEV)).contiguous()
+    g = torch.Generator(device="cpu").manual_seed(52)
+    k_new = torch.randn((len(ctx), count, Hkv, D), generator=g).to(dt).to(DEV)
+    v_new = torch.randn((len(ctx), count, Hkv, D), generator=g).to(dt).to(DEV)
+    K0, V0, B0 = f64(wl.k_pool), f64(wl.v_pool), f64(bounds)
+    rK, rV, rB = oracle.kv_commit(K0, V0, i32(wl.page_table), f64(k_new), f64(v_new), i32(first),
+                                  i32(committed), B0)
+    kvc = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, committed, wl.cfg["Hq"])
+    s3r.kv_commit(kvc, k_new, v_new, first, bounds)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(wl.k_pool), rK)
+    assert np.array_equal(f64(wl.v_pool), rV)
+    assert np.array_equal(f64(bounds), rB, equal_nan=True)
