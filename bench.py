@@ -17,7 +17,16 @@ bounds and logits each counted once) over the measured step time, in GB/s;
 `accepted_tokens_per_s` is committed tokens (accepted + 1 per sequence) per
 second. `roofline` covers the dominant launch (dense verify), timed with HIP
 events on the stream it runs on; `cpu_baseline` is the fp64 oracle on a
-bounded slice of the same workload, on the host.
+bounded slice of the same workload, on the host. `select_once` times the same
+round with one selection per round (s3r_sparse_draft_round at step 0, the
+later steps reusing it).
+
+--sweep instead measures the speedup condition over gamma x budget x
+acceptance x context at the 8B head shape: per point, the round (both
+selection frequencies), a dense single-query decode over the same KV (the
+one-layer autoregressive step), the committed tokens per round E, and the
+speedup E * t_dense / t_round next to the byte model's E * bytes_dense /
+bytes_round. One JSON line per point.
 """
 import argparse
 import json
@@ -43,6 +52,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough budget of oracle CPU work for the baseline")
+    p.add_argument("--sweep", action="store_true",
+                   help="speedup-condition sweep instead of the one-round measurement")
     return p.parse_args()
 
 
@@ -70,21 +81,16 @@ def step_bytes(cfg, ctx, select_once=False):
     return parts
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        sys.exit(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-                 "(the S3R hot path shards by sequence with no exchange; see DESIGN.md)")
+def build_round(config, dev, seed=0, **overrides):
+    """Buffers and launch closures of one round on a fresh seeded workload."""
+    import types
 
-    import numpy as np
     import torch
 
     import self_sparse_speculative_paged_amd as s3r
     from s3r_inputs import make_workload
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = make_workload(args.config, device=dev, seed=0)
+    wl = make_workload(config, device=dev, seed=seed, **overrides)
     cfg = wl.cfg
     B, Hq, Hkv, D, P, gamma, V = (cfg[k] for k in ("B", "Hq", "Hkv", "D", "P", "gamma", "V"))
     budget, T = cfg["budget"], cfg["temperature"]
@@ -102,6 +108,8 @@ def main():
     q_draft = [wl.draft_q(j) for j in range(gamma)]
     sel = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
     nsel = torch.empty((B,), dtype=torch.int32, device=dev)
+    sel_r = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    nsel_r = torch.empty((B,), dtype=torch.int32, device=dev)
     d_out = torch.empty((gamma, B, Hq, D), dtype=torch.bfloat16, device=dev)
     v_out = torch.empty((B, gamma + 1, Hq, D), dtype=torch.bfloat16, device=dev)
     ws_sel = torch.empty(max(1, s3r.page_select_workspace(kv, budget)), dtype=torch.uint8, device=dev)
@@ -133,10 +141,6 @@ def main():
         verify()
         sample(offset)
 
-    # Variant: select once per round (forced tail pages), reuse for steps 1..gamma-1.
-    sel_r = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
-    nsel_r = torch.empty((B,), dtype=torch.int32, device=dev)
-
     def one_round_select_once(offset=0):
         kv.set_seq_lens(wl.seq_lens[0])
         s3r.sparse_draft_round(kv, bounds, q_draft[0], budget, gamma, scale,
@@ -148,75 +152,120 @@ def main():
         verify()
         sample(offset)
 
+    # The one-layer autoregressive step: one query at position L-1 over all L tokens.
+    q_dense = wl.q_verify[:, :1].contiguous()
+    o_dense = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws_dense = torch.empty(max(1, s3r.attn_workspace(kv, 1, wl.max_pages)), dtype=torch.uint8,
+                           device=dev)
+
+    def dense_decode(offset=0):
+        kv.set_seq_lens(wl.seq_lens[0])
+        s3r.dense_verify_attn(kv, q_dense, scale, out=o_dense, workspace=ws_dense)
+
+    def accept_stats():
+        """Mean accepted drafts per sequence and committed tokens per round, over 8 offsets."""
+        acc = []
+        for off in range(8):
+            sample(off)
+            acc.append(n_acc.clone())
+        torch.cuda.synchronize()
+        acc = torch.stack(acc).float()
+        return float(acc.mean()), float((acc + 1).sum(dim=1).mean())
+
+    return types.SimpleNamespace(**locals())
+
+
+def make_runner(fn, graphed, keep):
+    """A replay of fn(0) captured into a HIP graph (kept alive in `keep`), or fn itself."""
+    import torch
+    if not graphed:
+        return lambda: fn(0)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        fn(0)
+    keep.append(g)
+    return g.replay
+
+
+def time_runner(runner, steps, warmup):
+    """Mean ms per call of `steps` back-to-back calls, synchronised on both sides."""
+    import torch
+    for _ in range(max(1, warmup)):
+        runner()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        runner()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.exit(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+                 "(the S3R hot path shards by sequence, with no exchange between GPUs)")
+    if args.sweep:
+        return sweep(args)
+
+    import torch
+
+    import self_sparse_speculative_paged_amd as s3r
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = build_round(args.config, dev, seed=0)
+    wl, cfg, kv, bounds = R.wl, R.cfg, R.kv, R.bounds
+    B, Hq, Hkv, D, P, gamma, V = R.B, R.Hq, R.Hkv, R.D, R.P, R.gamma, R.V
+    budget, scale, ctx = R.budget, R.scale, R.ctx
+
     # eager warm-up, and the accepted-length statistics over several Philox offsets
     for w in range(max(1, args.warmup)):
-        one_round(w)
-    acc = []
-    for off in range(8):
-        sample(off)
-        acc.append(n_acc.clone())
-    torch.cuda.synchronize()
-    acc = torch.stack(acc).float()
-    mean_committed = float((acc + 1).sum(dim=1).mean())  # tokens committed per round, all sequences
-
-    def make_runner(fn):
-        if args.no_graph:
-            return fn
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(s)
-        with torch.cuda.graph(g):
-            fn(0)
-        graphs.append(g)
-        return g.replay
-
-    def time_runner(runner):
-        for _ in range(max(1, args.warmup)):
-            runner()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(args.steps):
-            runner()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps
+        R.one_round(w)
+    mean_acc, mean_committed = R.accept_stats()
 
     graphs = []
-    ms = time_runner(make_runner(one_round))
-    ms_once = time_runner(make_runner(one_round_select_once))
+    ms = time_runner(make_runner(R.one_round, not args.no_graph, graphs), args.steps, args.warmup)
+    ms_once = time_runner(make_runner(R.one_round_select_once, not args.no_graph, graphs),
+                          args.steps, args.warmup)
 
-    # Per-launch timing of each entry point (eager, events on the launch stream).
+    # Per-launch time of each entry point: the call captured alone into a HIP
+    # graph and replayed back to back between two events on the launch stream
+    # (eager calls with --no-graph), so host launch latency stays out of it.
     def time_call(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for a, b in evs:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3  # us
+        return 1e3 * time_runner(make_runner(lambda _off: fn(), not args.no_graph, graphs), reps,
+                                 args.warmup)
 
     reps = max(5, args.steps)
     kv.set_seq_lens(wl.seq_lens[0])
-    t_select = time_call(lambda: s3r.page_select(kv, bounds, q_draft[0], budget, scale, sel, nsel,
-                                                 workspace=ws_sel), reps)
-    t_draft = time_call(lambda: s3r.sparse_draft_attn(kv, q_draft[0], sel, scale, out=d_out[0],
-                                                      workspace=ws_d), reps)
-    t_bounds = time_call(lambda: s3r.page_bounds_update(kv, bounds, first_pos=first_pos[0],
+    t_select = time_call(lambda: s3r.page_select(kv, bounds, R.q_draft[0], budget, scale, R.sel,
+                                                 R.nsel, workspace=R.ws_sel), reps)
+    t_draft = time_call(lambda: s3r.sparse_draft_attn(kv, R.q_draft[0], R.sel, scale,
+                                                      out=R.d_out[0], workspace=R.ws_d), reps)
+    t_bounds = time_call(lambda: s3r.page_bounds_update(kv, bounds, first_pos=R.first_pos[0],
                                                         max_pages_touched=1), reps)
-    t_step = time_call(lambda: s3r.sparse_draft_step(kv, bounds, q_draft[0], budget, scale,
-                                                     refresh_from=first_pos[0], selected=sel,
-                                                     num_selected=nsel, out=d_out[0],
-                                                     workspace=ws_step), reps)
+    t_step = time_call(lambda: s3r.sparse_draft_step(kv, bounds, R.q_draft[0], budget, scale,
+                                                     refresh_from=R.first_pos[0], selected=R.sel,
+                                                     num_selected=R.nsel, out=R.d_out[0],
+                                                     workspace=R.ws_step), reps)
     kv.set_seq_lens(wl.seq_lens[gamma])
-    t_verify = time_call(lambda: s3r.dense_verify_attn(kv, wl.q_verify, scale, out=v_out,
-                                                       workspace=ws_v), reps)
-    t_sample = time_call(lambda: sample(0), reps)
+    t_verify = time_call(lambda: s3r.dense_verify_attn(kv, wl.q_verify, scale, out=R.v_out,
+                                                       workspace=R.ws_v), reps)
+    t_sample = time_call(lambda: R.sample(0), reps)
+    # KV commit of a verify's gamma+1 rows at the round's positions (last: it rewrites them).
+    g = torch.Generator(device=dev).manual_seed(1)
+    k_new = torch.randn((B, gamma + 1, Hkv, D), device=dev, generator=g).to(wl.k_pool.dtype)
+    v_new = torch.randn((B, gamma + 1, Hkv, D), device=dev, generator=g).to(wl.k_pool.dtype)
+    kv.set_seq_lens(wl.seq_lens[gamma])
+    t_commit = time_call(lambda: s3r.kv_commit(kv, k_new, v_new, R.first_pos[0], bounds), reps)
 
     parts = step_bytes(cfg, ctx)
     total_bytes = sum(parts.values())
@@ -248,14 +297,15 @@ def main():
                    "graph": not args.no_graph},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "accepted_tokens_per_s": round(mean_committed / (ms * 1e-3), 1),
-        "mean_accepted_per_seq": round(float(acc.mean()), 3),
+        "mean_accepted_per_seq": round(mean_acc, 3),
         "draft_verify_kv_gbs": round(dv_gbs, 1),
         "draft_kv_gbs": round(draft_gbs, 1),
         "verify_kv_gbs": round(verify_gbs, 1),
         "step_bytes": {k2: int(v2) for k2, v2 in parts.items()},
         "launch_us": {"page_bounds_update": round(t_bounds, 2), "page_select": round(t_select, 2),
                       "sparse_draft_attn": round(t_draft, 2), "sparse_draft_step": round(t_step, 2),
-                      "dense_verify_attn": round(t_verify, 2), "spec_sample": round(t_sample, 2)},
+                      "dense_verify_attn": round(t_verify, 2), "spec_sample": round(t_sample, 2),
+                      "kv_commit": round(t_commit, 2)},
         "select_once": {
             "ms_per_step": round(ms_once, 4),
             "value": round(sum(parts_once.values()) / (ms_once * 1e-3) / 1e9, 1),
@@ -270,6 +320,53 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+SWEEP_CONTEXTS = (8192, 32768)
+SWEEP_GAMMAS = (2, 4, 8)
+SWEEP_NOISE = (0.5, 1.35)      # target-logit noise: per-token acceptance about 0.8 and 0.5
+SWEEP_BUDGETS = (512, 2048)
+
+
+def sweep(args):
+    """Speedup condition over context x gamma x acceptance x budget (8B heads, batch 32)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for L in SWEEP_CONTEXTS:
+        for gamma in SWEEP_GAMMAS:
+            for noise in SWEEP_NOISE:
+                for budget in SWEEP_BUDGETS:
+                    R = build_round("qwen3_8b", dev, seed=0, L=L, gamma=gamma, noise_sd=noise,
+                                    budget=budget)
+                    mean_acc, mean_committed = R.accept_stats()
+                    E = mean_committed / R.B
+                    graphs = []
+                    ms = time_runner(make_runner(R.one_round, True, graphs), args.steps, args.warmup)
+                    ms_once = time_runner(make_runner(R.one_round_select_once, True, graphs),
+                                          args.steps, args.warmup)
+                    ms_dense = time_runner(make_runner(R.dense_decode, True, graphs), args.steps,
+                                           args.warmup)
+                    kv_tok = 2 * R.Hkv * R.D * 2
+                    dense_bytes = R.B * L * kv_tok
+                    round_bytes = sum(step_bytes(R.cfg, R.ctx).values())
+                    once_bytes = sum(step_bytes(R.cfg, R.ctx, select_once=True).values())
+                    print(json.dumps({
+                        "sweep_point": {"context": L, "gamma": gamma, "budget_tokens": budget,
+                                        "target_noise_sd": noise},
+                        "mean_accepted": round(mean_acc, 3), "committed_per_round": round(E, 3),
+                        "round_ms": round(ms, 4), "round_select_once_ms": round(ms_once, 4),
+                        "dense_decode_ms": round(ms_dense, 4),
+                        "speedup": round(E * ms_dense / ms, 3),
+                        "speedup_select_once": round(E * ms_dense / ms_once, 3),
+                        "speedup_bytes": round(E * dense_bytes / round_bytes, 3),
+                        "speedup_bytes_select_once": round(E * dense_bytes / once_bytes, 3),
+                        "round_gbs": round(round_bytes / (ms * 1e-3) / 1e9, 1),
+                        "dense_gbs": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+                    }), flush=True)
+                    del R, graphs
+                    torch.cuda.empty_cache()
 
 
 def read_counter_traffic(config):

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void bounds_kernel(BoundsArgs a) {
 // head; a wave scores 64/(D/8) pages per step.
 // ---------------------------------------------------------------------------
 template <typename T, int kD, int kG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kG <= 4 ? 4 : 2, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kG <= 2 ? 4 : (kG <= 4 ? 3 : 2), 8)))
 void score_kernel(SelectArgs a) {
   constexpr int kLpp = kD / 8;            // lanes per page (8 d per lane)
   constexpr int kGroups = 256 / kLpp;     // page groups per block
