@@ -228,8 +228,12 @@ __device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
 
 // One row block (the draft, small verify groups) fits two waves per SIMD with a
 // 2-stage pipeline; more row blocks run one wave per SIMD with deeper stages.
+// Register pipeline depth per row-block count: what fits the registers of one
+// wave per SIMD (two waves for one row block) without spilling. Four row
+// blocks hold 64 rows of accumulators and queries; a second stage spills there
+// and runs 2.5x slower than a single one.
 template <int kNB>
-constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : 2); }
+constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : (kNB == 3 ? 2 : 1)); }
 template <int kNB>
 constexpr int bf16_waves_per_simd() { return kNB == 1 ? 2 : 1; }
 

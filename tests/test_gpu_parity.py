@@ -61,6 +61,7 @@ VERIFY_CASES = [
     ("bf16", 128, 4, 2, 6, (1000, 515, 129)),    # 28 rows: two row blocks (Qwen3-8B heads)
     ("bf16", 128, 4, 2, 8, (777, 64)),           # 36 rows: three row blocks
     ("bf16", 64, 8, 1, 7, (400, 95)),            # 64 rows: four row blocks, D=64
+    ("bf16", 128, 8, 1, 7, (300, 77)),           # 64 rows at D=128: the one-stage pipeline
     ("bf16", 64, 2, 3, 3, (48, 2049)),
 ]
 
