@@ -4,8 +4,10 @@ bench.py times (same split plan, same workspaces), checked on sampled
 
 Per workload: the first draft step (the fused tail-page bounds refresh, page
 select and sparse draft attention, as bench.py runs it), the dense verify of
-gamma + 1 queries, and the speculative sampling of every sequence. Tolerances
-as in test_gpu_parity.py.
+gamma + 1 queries, the speculative sampling of every sequence, the round's
+once-per-round selection reused at its last draft step (bench.py's
+select_once), and a KV commit of the verify's gamma + 1 rows at the accepted
+lengths. Tolerances as in test_gpu_parity.py; the commit is bit-exact.
 """
 import math
 
@@ -92,6 +94,66 @@ def _run_fullsize(name, samples, shrink_to=None):
         rv = oracle.dense_verify_attn(qv, K, V, pt, np.array([L + gamma]), scale)
         err_v = np.max(np.abs(v_out[b, :, heads].cpu().numpy() - rv[0]))
         assert err_v <= 1e-2, (name, b, h, "verify", err_v)
+
+    # once-per-round selection at step 0, reused at the round's last step
+    kv.set_seq_lens(wl.seq_lens[0])
+    _, rsel_g, rnsel_g = s3r.sparse_draft_round(kv, bounds, q0, budget, gamma, scale,
+                                                refresh_from=(wl.seq_lens[0] - 1).contiguous())
+    kv.set_seq_lens(wl.seq_lens[gamma - 1])
+    q_last = wl.draft_q(gamma - 1)
+    last_out = s3r.sparse_draft_attn(kv, q_last, rsel_g, scale)
+    torch.cuda.synchronize()
+    for b, h in samples:
+        if b >= B:
+            continue
+        L = int(wl.ctx[b])
+        K, V, pt = _slice(wl, b, h, G)
+        heads = slice(h * G, (h + 1) * G)
+        rb = oracle.page_bounds(K, pt, np.array([L]))
+        qd = q0[b:b + 1, heads].to("cpu", torch.float64).numpy()
+        rsel, rn, rsc = oracle.page_select_round(rb, qd, pt, np.array([L]), budget, gamma, scale, P)
+        g = [int(x) for x in rsel_g[b, h].cpu() if x >= 0]
+        r = [int(x) for x in rsel[0, 0] if x >= 0]
+        assert int(rnsel_g[b]) == int(rn[0]) and len(g) == len(r), (name, b, h, "round select")
+        forced = oracle.round_forced_pages(L, gamma, P, pt.shape[1])
+        assert set(forced) <= set(g), (name, b, h, forced)
+        if g != r:
+            sc = rsc[(0, 0)]
+            kth = sorted(sc.values(), reverse=True)[k - len(forced) - 1]
+            assert all(abs(sc[j] - kth) <= 1e-4 for j in set(g) ^ set(r)), (name, b, h)
+        ql = q_last[b:b + 1, heads].to("cpu", torch.float64).numpy()
+        rl = oracle.sparse_draft_attn(ql, K, V, pt, np.array([L + gamma - 1]),
+                                      rsel_g[b:b + 1, h:h + 1].cpu().numpy(), scale)
+        err_l = np.max(np.abs(last_out[b, heads].cpu().numpy() - rl[0]))
+        assert err_l <= 1e-2, (name, b, h, "round draft", err_l)
+
+    # KV commit of gamma + 1 rows from the round's first position, kept up to
+    # the accepted length (the rest rolled back)
+    first = (wl.seq_lens[0] - 1).contiguous()
+    committed = (wl.seq_lens[0] + nacc).contiguous()
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    k_new = torch.randn((B, gamma + 1, Hkv, D), device="cuda", generator=gen).to(wl.k_pool.dtype)
+    v_new = torch.randn((B, gamma + 1, Hkv, D), device="cuda", generator=gen).to(wl.k_pool.dtype)
+    before = {}
+    for b, h in samples:
+        if b < B:
+            K, V, pt = _slice(wl, b, h, G)
+            n = pt.shape[1]
+            phys = wl.page_table[b, :n].long()
+            before[(b, h)] = (K, V, pt, bounds.index_select(0, phys)[:, h:h + 1].double().cpu().numpy())
+    kv.set_seq_lens(committed)
+    s3r.kv_commit(kv, k_new, v_new, first, bounds)
+    torch.cuda.synchronize()
+    for (b, h), (K, V, pt, B0) in before.items():
+        K2, V2, _ = _slice(wl, b, h, G)
+        phys = wl.page_table[b, :pt.shape[1]].long()
+        B2 = bounds.index_select(0, phys)[:, h:h + 1].double().cpu().numpy()
+        rK, rV, rB = oracle.kv_commit(K, V, pt, k_new[b:b + 1, :, h:h + 1].double().cpu().numpy(),
+                                      v_new[b:b + 1, :, h:h + 1].double().cpu().numpy(),
+                                      first[b:b + 1].cpu().numpy(), committed[b:b + 1].cpu().numpy(),
+                                      B0)
+        assert np.array_equal(K2, rK) and np.array_equal(V2, rV), (name, b, h, "commit rows")
+        assert np.array_equal(B2, rB, equal_nan=True), (name, b, h, "commit bounds")
 
     ro, rn, dec = oracle.spec_sample(wl.draft_logits.double().cpu().numpy(),
                                      wl.target_logits.double().cpu().numpy(),
