@@ -37,6 +37,15 @@ s3r_status check_workspace(void* ws, size_t have, size_t need) {
 
 s3r_status from_hip(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of one attention call: the split partials, then (ragged batches)
+// the longest-first order.
+size_t attn_call_workspace(const s3r_paged_kv& kv, const s3r::SplitPlan& plan) {
+  const size_t ob = s3r::order_bytes(kv);
+  return ob ? align256(plan.workspace_bytes) + ob : plan.workspace_bytes;
+}
+
 s3r::AttnArgs attn_args(const s3r_paged_kv* kv, const s3r::SplitPlan& plan, const void* q,
                         const int32_t* sel, int32_t ksel, int32_t n_q, float scale,
                         s3r_dtype out_dtype, void* out, void* ws);
@@ -57,8 +66,10 @@ s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* s
   if (s3r_status s = check_attention(kv, q, n_q, scale, out_dtype, out)) return s;
   const int32_t max_items = sel ? ksel : kv->max_pages_per_seq;
   const s3r::SplitPlan plan = s3r::plan_attention(*kv, n_q, max_items);
-  if (s3r_status s = check_workspace(ws, ws_bytes, plan.workspace_bytes)) return s;
-  const s3r::AttnArgs a = attn_args(kv, plan, q, sel, ksel, n_q, scale, out_dtype, out, ws);
+  if (s3r_status s = check_workspace(ws, ws_bytes, attn_call_workspace(*kv, plan))) return s;
+  s3r::AttnArgs a = attn_args(kv, plan, q, sel, ksel, n_q, scale, out_dtype, out, ws);
+  if (s3r::order_bytes(*kv))
+    a.order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align256(plan.workspace_bytes));
   return from_hip(s3r::launch_attention(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -149,6 +160,7 @@ struct DraftStepPlan {
   size_t select_ws;
   bool fused;
   int32_t list_offset;
+  size_t order_offset;     // longest-first order in the workspace (ragged batches)
   size_t workspace_bytes;  // enough for every path the call may take
 };
 
@@ -167,6 +179,10 @@ DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
             list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
   p.workspace_bytes = p.fused ? p.select_ws + p.attn.workspace_bytes
                               : (p.select_ws > p.attn.workspace_bytes ? p.select_ws : p.attn.workspace_bytes);
+  if (const size_t ob = s3r::order_bytes(kv)) {
+    p.order_offset = align256(p.workspace_bytes);
+    p.workspace_bytes = p.order_offset + ob;
+  }
   return p;
 }
 
@@ -226,7 +242,7 @@ size_t s3r_page_select_workspace(const s3r_paged_kv* kv, int32_t budget_tokens) 
 
 size_t s3r_attn_workspace(const s3r_paged_kv* kv, int32_t n_queries, int32_t max_pages_attended) {
   if (check_kv(kv) != S3R_OK || n_queries < 1 || max_pages_attended < 1) return 0;
-  return s3r::plan_attention(*kv, n_queries, max_pages_attended).workspace_bytes;
+  return attn_call_workspace(*kv, s3r::plan_attention(*kv, n_queries, max_pages_attended));
 }
 
 size_t s3r_spec_sample_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab) {
@@ -304,6 +320,9 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
   if (s3r_status s = check_workspace(workspace, workspace_bytes, plan.workspace_bytes)) return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t k = budget_tokens / kv->page_size;
+  int32_t* order = s3r::order_bytes(*kv)
+                       ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_offset)
+                       : nullptr;
   s3r::SelectArgs sa = select_args(kv, bounds, q, budget_tokens, softmax_scale, selected,
                                    num_selected, workspace);
   sa.round_gamma = round_gamma;
@@ -320,6 +339,7 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
     a.refresh_from = refresh_from;
     a.sel_scale = softmax_scale;
     a.round_gamma = round_gamma;
+    a.order = order;
     return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
   }
   if (plan.fused) {
@@ -334,6 +354,7 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
     a.nsel_out = num_selected;
     a.list_offset = plan.list_offset;
     a.round_gamma = round_gamma;
+    a.order = order;
     return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
   }
   // Unfused: bounds refresh, then select, then attention (stream order makes
@@ -354,8 +375,9 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
     if (hipError_t e = s3r::launch_bounds(ba, kv->kv_dtype, st)) return from_hip(e);
   }
   if (hipError_t e = s3r::launch_select(sa, kv->kv_dtype, st)) return from_hip(e);
-  const s3r::AttnArgs a = attn_args(kv, plan.attn, q, selected, k, 1, softmax_scale, out_dtype, out,
-                                    plan.attn.workspace_bytes ? workspace : nullptr);
+  s3r::AttnArgs a = attn_args(kv, plan.attn, q, selected, k, 1, softmax_scale, out_dtype, out,
+                              plan.attn.workspace_bytes ? workspace : nullptr);
+  a.order = order;
   return from_hip(s3r::launch_attention(a, kv->kv_dtype, st));
 }
 

@@ -31,6 +31,20 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Pages per split of one (sequence, kv head) with n_items pages to attend: its
+// pages spread evenly over all waves_per_group * n_groups splits, so a short
+// sequence keeps every wave of its workgroup busy instead of leaving one long
+// split to a single wave. At least 16 pages (fewer only if the plan's split is
+// smaller) and at most the plan's split, which sizes the LDS window tables.
+// Even, so windows of two pages never straddle splits.
+__device__ __forceinline__ int split_pages(const AttnArgs& a, int n_items) {
+  const int splits = a.waves_per_group * a.n_groups;
+  int pps = (n_items + splits - 1) / splits;
+  pps = (pps + 1) & ~1;
+  const int lo = min(16, a.pages_per_split);
+  return min(a.pages_per_split, max(lo, pps));
+}
+
 // Resolves the two logical pages of a window to physical pages. Invalid pages
 // (past the range, -1 in a selection, or past the sequence) alias a valid page
 // so every load stays in bounds; their tokens are masked.
@@ -331,16 +345,19 @@ void attn_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const int wave = kW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = blockIdx.x % a.n_groups;
-  const int bh = blockIdx.x / a.n_groups;
-  const int h = bh % a.Hkv, b = bh / a.Hkv;
+  const int slot = blockIdx.x / a.n_groups;
+  const int h = slot % a.Hkv;
+  const int b = a.order ? a.order[slot / a.Hkv] : slot / a.Hkv;
+  const int bh = b * a.Hkv + h;
   const int seq_len = a.seq_lens[b];
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
-  const int g0 = group * kW * a.pages_per_split;
+  const int pps = split_pages(a, n_items);
+  const int g0 = group * kW * pps;
   // the global combine skips an empty group (group 0 still publishes the selection)
   if (g0 >= n_items && a.n_groups > 1 && !(kSelect != kSelGiven && group == 0)) return;
-  const int j0 = g0 + wave * a.pages_per_split;
-  const int j1 = min(j0 + a.pages_per_split, n_items);
+  const int j0 = g0 + wave * pps;
+  const int j1 = min(j0 + pps, n_items);
   const bool active = j0 < n_items;
 
   extern __shared__ int4 lds[];
@@ -517,14 +534,16 @@ template <int kD, int kNB, bool kSparse>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x % a.n_groups;
-  const int bh = blockIdx.x / a.n_groups;
-  const int h = bh % a.Hkv, b = bh / a.Hkv;
+  const int slot = blockIdx.x / a.n_groups;
+  const int h = slot % a.Hkv;
+  const int b = a.order ? a.order[slot / a.Hkv] : slot / a.Hkv;
   const int seq_len = a.seq_lens[b];
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
-  const int j0 = split * a.pages_per_split;
+  const int pps = split_pages(a, n_items);
+  const int j0 = split * pps;
   if (j0 >= n_items) return;
-  const int j1 = min(j0 + a.pages_per_split, n_items);
+  const int j1 = min(j0 + pps, n_items);
 
   const float* kp = static_cast<const float*>(a.k_pool);
   const float* vp = static_cast<const float*>(a.v_pool);
@@ -597,6 +616,30 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Longest-first order: order[r] = the sequence of rank r by (length desc, index
+// asc). Thread b counts the sequences ranked before it over the lengths staged
+// in LDS, 1024 at a time.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void order_by_length_kernel(const int32_t* seq_lens, int B,
+                                                              int32_t* order) {
+  __shared__ int32_t lens[1024];
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  const int L = b < B ? seq_lens[b] : 0;
+  int rank = 0;
+  for (int c0 = 0; c0 < B; c0 += 1024) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < 1024 && c0 + c < B; c += 256) lens[c] = seq_lens[c0 + c];
+    __syncthreads();
+    const int n = min(1024, B - c0);
+    for (int c = 0; c < n; ++c) {
+      const int Lc = lens[c];
+      rank += (Lc > L) || (Lc == L && c0 + c < b);
+    }
+  }
+  if (b < B) order[rank] = b;
+}
+
+// ---------------------------------------------------------------------------
 // Split-KV combine: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // One wave per (sequence, query, q head) output row.
 // ---------------------------------------------------------------------------
@@ -610,7 +653,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   const int seq_len = a.seq_lens[b];
   const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   const int n_items = kSparse ? min(a.ksel, n_pages) : n_pages;
-  const int per_group = a.pages_per_split * a.waves_per_group;
+  const int per_group = split_pages(a, n_items) * a.waves_per_group;
   const int ns = (n_items + per_group - 1) / per_group;
   const size_t item0 = ((size_t)b * a.Hkv + h) * a.n_groups;
 
@@ -774,6 +817,11 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
 }
 
 hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream) {
+  if (a.order != nullptr) {
+    hipLaunchKernelGGL(order_by_length_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0,
+                       stream, a.seq_lens, a.B, a.order);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
   if (a.scores != nullptr || a.score_here) {  // fused draft step: bf16, one row block
     if (kv_dtype != S3R_BF16 || a.rows > 16) return hipErrorInvalidValue;
     return a.D == 128 ? launch_fused_draft<128>(a, stream) : launch_fused_draft<64>(a, stream);

@@ -77,7 +77,22 @@ struct AttnArgs {
   void* bounds_out;
   const int32_t* refresh_from;
   float sel_scale;
+  // Longest-first scheduling for ragged batches: when set, launch_attention
+  // first ranks the sequences by length into order[B] (device scratch the
+  // caller's workspace provides) and workgroup slots take sequences in that
+  // order, so the longest start first and the short ones fill in behind.
+  int32_t* order;
 };
+
+// Whether a batch is ragged enough for longest-first scheduling: its longest
+// table is more than twice the average the caller's page hint implies.
+inline bool schedule_longest_first(const s3r_paged_kv& kv) {
+  return kv.total_pages_hint > 0 &&
+         (int64_t)kv.max_pages_per_seq * kv.num_seqs > 2 * (int64_t)kv.total_pages_hint;
+}
+inline size_t order_bytes(const s3r_paged_kv& kv) {
+  return schedule_longest_first(kv) ? (sizeof(int32_t) * (size_t)kv.num_seqs + 255) & ~(size_t)255 : 0;
+}
 
 hipError_t launch_attention(const AttnArgs& a, s3r_dtype kv_dtype, hipStream_t stream);
 

@@ -423,3 +423,32 @@ def test_kv_commit_matches_oracle(kv, D, Hkv, ctx, count, slack, accepted):
     assert np.array_equal(f64(wl.k_pool), rK)
     assert np.array_equal(f64(wl.v_pool), rV)
     assert np.array_equal(f64(bounds), rB, equal_nan=True)
+
+
+def test_ragged_longest_first_matches_oracle():
+    """A ragged batch with its page hint set: the attention workgroups take the
+    sequences longest first (verify and the draft step)."""
+    ctx = (5000, 40, 700, 17, 2300, 64)
+    gamma, budget = 4, 256
+    wl = _make(_cfg("bf16", 128, 4, 2, gamma=gamma, budget=budget), list(ctx), seed=61)
+    total = sum(-(-(L + gamma) // 16) for L in ctx)
+    assert wl.max_pages * len(ctx) > 2 * total  # ragged enough to reorder
+    scale = 1.0 / np.sqrt(128)
+    K, V, pt = f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table)
+    out = s3r.dense_verify_attn(_kv(wl, gamma, hint=total), wl.q_verify, scale)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify_attn(f64(wl.q_verify), K, V, pt, i32(wl.seq_lens[gamma]), scale)
+    _check_attn(out, ref, "bf16")
+    bounds = torch.empty((wl.k_pool.shape[0], 2, 2, 128), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(_kv(wl, 0), bounds)
+    kv0 = _kv(wl, 0, hint=total)
+    q0 = wl.draft_q(0)
+    d_out, sel, nsel = s3r.sparse_draft_step(kv0, bounds, q0, budget, scale,
+                                             refresh_from=(wl.seq_lens[0] - 1).contiguous())
+    torch.cuda.synchronize()
+    L0 = i32(wl.seq_lens[0])
+    rb = oracle.page_bounds(K, pt, L0)
+    rsel, rn, rsc = oracle.page_select(rb, f64(q0), pt, L0, budget, scale)
+    check_pages(i32(sel), i32(nsel), rsel, rn, rsc, budget // 16)
+    ref = oracle.sparse_draft_attn(f64(q0), K, V, pt, L0, i32(sel), scale)
+    _check_attn(d_out, ref, "bf16")
