@@ -132,3 +132,17 @@ def test_split_plan_workspace_scales_with_hint():
     hinted = lib.s3r_attn_workspace(
         ctypes.byref(_kv(max_pages_per_seq=4096, num_seqs=8, total_pages_hint=8 * 600)), 5, 4096)
     assert hinted >= full  # a smaller average length means shorter splits, more of them
+
+
+def test_ragged_hint_reserves_the_longest_first_order():
+    """Once the page hint drops below half of B * max_pages (a ragged batch), the
+    attention and draft-step workspaces also hold the sequence order: B int32,
+    256-byte aligned. Hints either side of that line give the same split plan."""
+    lib = _lib.load()
+    B, maxp = 300, 4096
+    even = ctypes.byref(_kv(max_pages_per_seq=maxp, num_seqs=B, total_pages_hint=B * maxp // 2))
+    ragged = ctypes.byref(_kv(max_pages_per_seq=maxp, num_seqs=B, total_pages_hint=B * maxp // 2 - 1))
+    order = (4 * B + 255) // 256 * 256
+    assert lib.s3r_attn_workspace(ragged, 5, maxp) >= lib.s3r_attn_workspace(even, 5, maxp) + order
+    assert (lib.s3r_sparse_draft_step_workspace(ragged, 2048)
+            >= lib.s3r_sparse_draft_step_workspace(even, 2048) + order)
