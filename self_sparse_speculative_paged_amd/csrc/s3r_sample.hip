@@ -14,9 +14,10 @@
 //             accumulated in fp64;
 //   decide:   per sequence, fold the row statistics and run the accept scan;
 //   residual: per (sequence, chunk) sum the chunk's residual (or bonus)
-//             weights in fp64;
-//   finalize: per sequence, locate the chunk holding u * sum(w), then the token
-//             inside it by an ordered block scan; write the round's tokens.
+//             weights in fp64, per 16-token run and per chunk;
+//   finalize: per sequence, locate the chunk holding u * sum(w), then the
+//             16-token run inside it, then the token, each by an ordered wave
+//             scan; write the round's tokens.
 // Uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) at key
 // (seed, 0), counter (offset, b, slot, stream); u = (word0 >> 11) * 2^-53.
 #include <math.h>
@@ -29,7 +30,7 @@ namespace {
 
 constexpr int kChunk = 4096;
 constexpr int kThreads = 256;
-constexpr int kPerThread = kChunk / kThreads;
+constexpr int kPerThread = kChunk / kThreads;  // also the tokens of one residual run
 
 // Philox4x64-10 round multipliers and Weyl key increments (Salmon et al.).
 constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
@@ -60,6 +61,8 @@ struct Layout {
   double* sum;     // [B][R][C] chunk sum of exp((x - chunk max) / T)
   double* wsum;    // [B][C] chunk sum of the residual/bonus weights
   double* psum;    // [B][C] chunk sum of the target row's probabilities
+  double* wrun;    // [B][C][kThreads] the same over each 16-token run
+  double* prun;    // [B][C][kThreads]
   double* iz;      // [B][R] 1 / row normaliser, as the residual pass used it
   float* cmax;     // [B][R][C] chunk max logit
   float* rmax;     // [B][R] row max logit
@@ -76,6 +79,10 @@ __host__ __device__ inline Layout layout_of(void* ws, int B, int gamma, int C) {
   p += sizeof(double) * B * C;
   l.psum = reinterpret_cast<double*>(p);
   p += sizeof(double) * B * C;
+  l.wrun = reinterpret_cast<double*>(p);
+  p += sizeof(double) * B * C * kThreads;
+  l.prun = reinterpret_cast<double*>(p);
+  p += sizeof(double) * B * C * kThreads;
   l.iz = reinterpret_cast<double*>(p);
   p += sizeof(double) * B * R;
   l.cmax = reinterpret_cast<float*>(p);
@@ -271,29 +278,62 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
   load_decision(a, b, rd);
   const float c_log2 = 1.4426950408889634f / a.temperature;
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
-  // All of this thread's logits are loaded before any is used.
   const int tr = a.gamma + rd.n, dr = rd.n < a.gamma ? rd.n : tr;
   const float* trow = row_ptr(a, b, tr);
   const float* drow = row_ptr(a, b, dr);
+  // Coalesced as in the stats pass: load k of thread t covers tokens
+  // lo + 4 * (t + kThreads * k) .. + 3. A run of 16 consecutive tokens is then
+  // four adjacent lanes of one load, folded by a fixed quad reduction.
+  const bool vec = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15) == 0;
   float xt[kPerThread], xd[kPerThread];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int t = lo + threadIdx.x + kThreads * k;
-    xt[k] = t < hi ? trow[t] : -__builtin_huge_valf();
-    xd[k] = t < hi ? drow[t] : -__builtin_huge_valf();
+  for (int k = 0; k < kPerThread / 4; ++k) {
+    const int t = lo + 4 * (threadIdx.x + kThreads * k);
+    if (vec && t + 3 < hi) {
+      const f32x4 vt = load_nt16<f32x4>(trow + t);
+      const f32x4 vd = load_nt16<f32x4>(drow + t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xt[4 * k + e] = vt[e];
+        xd[4 * k + e] = vd[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xt[4 * k + e] = t + e < hi ? trow[t + e] : -__builtin_huge_valf();
+        xd[4 * k + e] = t + e < hi ? drow[t + e] : -__builtin_huge_valf();
+      }
+    }
   }
   const bool bonus = rd.n == a.gamma;
+  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
+  double* wrun = L.wrun + ((size_t)b * a.n_chunks + c) * kThreads;
+  double* prun = L.prun + ((size_t)b * a.n_chunks + c) * kThreads;
   double w = 0.0, ps = 0.0;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const double p = (double)scaled_exp(xt[k], rd.M[tr], c_log2) * rd.iZ[tr];
-    const double q = bonus ? 0.0 : (double)scaled_exp(xd[k], rd.M[dr], c_log2) * rd.iZ[dr];
-    w += p > q ? p - q : 0.0;
-    ps += p;
+  for (int k = 0; k < kPerThread / 4; ++k) {
+    double wk = 0.0, pk = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // token order
+      const double p = (double)scaled_exp(xt[4 * k + e], rd.M[tr], c_log2) * rd.iZ[tr];
+      const double q = bonus ? 0.0 : (double)scaled_exp(xd[4 * k + e], rd.M[dr], c_log2) * rd.iZ[dr];
+      wk += p > q ? p - q : 0.0;
+      pk += p;
+    }
+    w += wk;
+    ps += pk;
+    wk += __shfl_xor(wk, 1, 64);
+    pk += __shfl_xor(pk, 1, 64);
+    wk += __shfl_xor(wk, 2, 64);
+    pk += __shfl_xor(pk, 2, 64);
+    if ((threadIdx.x & 3) == 0) {
+      const int r = (kThreads / 4) * k + threadIdx.x / 4;  // run index inside the chunk
+      wrun[r] = wk;
+      prun[r] = pk;
+    }
   }
   w = block_reduce_sum<double>(w, redd);
   ps = block_reduce_sum<double>(ps, redd);
-  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
   if (threadIdx.x == 0) {
     L.wsum[(size_t)b * a.n_chunks + c] = w;
     L.psum[(size_t)b * a.n_chunks + c] = ps;
@@ -316,7 +356,6 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
 // contiguous 64-token runs of the chosen chunk; running sums are ordered wave
 // scans, so the draw is deterministic.
 constexpr int kFinalizeLanes = 64;
-constexpr int kTokPerLane = kChunk / kFinalizeLanes;
 
 __global__ __launch_bounds__(kFinalizeLanes) void finalize_kernel(SampleArgs a) {
   const int b = blockIdx.x, lane = threadIdx.x;
@@ -378,37 +417,58 @@ __global__ __launch_bounds__(kFinalizeLanes) void finalize_kernel(SampleArgs a) 
   const unsigned long long owner = __ballot(chunk == best);
   const double base = fallback ? 0.0 : __shfl(before, owner ? __ffsll(owner) - 1 : 0, 64);
 
-  // Token level inside the chosen chunk.
-  const int lo = best * kChunk, hi = min(a.V, lo + kChunk);
-  const int t0 = min(hi, lo + kTokPerLane * lane), t1 = min(hi, t0 + kTokPerLane);
+  // Run level inside the chosen chunk: lane l scans runs 4l .. 4l+3. Rounding
+  // can leave the target past the runs' total; then (as for chunks) the last
+  // run with mass is taken.
+  const double* runs = (use_p ? L.prun : L.wrun) + ((size_t)b * a.n_chunks + best) * kThreads;
+  double rw[kThreads / 64], rown = 0.0;
+#pragma unroll
+  for (int e = 0; e < kThreads / 64; ++e) {
+    rw[e] = runs[(kThreads / 64) * lane + e];
+    rown += rw[e];
+  }
+  const double rincl = wave_inclusive_scan(rown);
+  double rrun = base + rincl - rown;
+  int rfirst = 0x7fffffff, rlast = -1;
+  double rbefore = 0.0;
+#pragma unroll
+  for (int e = 0; e < kThreads / 64; ++e) {
+    const int r = (kThreads / 64) * lane + e;
+    if (rw[e] > 0.0) rlast = r;
+    if (rfirst == 0x7fffffff && !fallback && rrun + rw[e] > target) {
+      rfirst = r;
+      rbefore = rrun;
+    }
+    rrun += rw[e];
+  }
+  int rsel = rfirst;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) rsel = min(rsel, __shfl_xor(rsel, x, 64));
+  const bool rfall = rsel == 0x7fffffff;
+  if (rfall) {
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) rlast = max(rlast, __shfl_xor(rlast, x, 64));
+    rsel = max(rlast, 0);
+  }
+  const unsigned long long rowner = __ballot(rfirst == rsel);
+  const double rbase = rfall ? 0.0 : __shfl(rbefore, rowner ? __ffsll(rowner) - 1 : 0, 64);
+
+  // Token level: lanes 0..15 take the run's 16 tokens.
   const float c_log2 = 1.4426950408889634f / a.temperature;
+  const int lo = best * kChunk, hi = min(a.V, lo + kChunk);
+  const int t = lo + kPerThread * rsel + (lane & (kPerThread - 1));
+  const bool mine = lane < kPerThread && t < hi;
   const float* trow = row_ptr(a, b, tr);
   const float* drow = row_ptr(a, b, dr);
-  float xt[kTokPerLane], xd[kTokPerLane];
-#pragma unroll
-  for (int k = 0; k < kTokPerLane; ++k) {
-    const int t = t0 + k;
-    xt[k] = t < t1 ? trow[t] : -__builtin_huge_valf();
-    xd[k] = t < t1 ? drow[t] : -__builtin_huge_valf();
-  }
-  double w[kTokPerLane];
-  double local = 0.0;
-#pragma unroll
-  for (int k = 0; k < kTokPerLane; ++k) {
-    const double p = (double)scaled_exp(xt[k], Mt, c_log2) * iZt;
-    const double q = bonus ? 0.0 : (double)scaled_exp(xd[k], Md, c_log2) * iZd;
-    w[k] = use_p ? p : (p > q ? p - q : 0.0);
-    local += w[k];
-  }
-  const double tincl = wave_inclusive_scan(local);
-  double run = base + tincl - local;
-  int first = 0x7fffffff, last = -1;
-#pragma unroll
-  for (int k = 0; k < kTokPerLane; ++k) {
-    if (w[k] > 0.0) last = t0 + k;
-    run += w[k];
-    if (first == 0x7fffffff && !fallback && run > target) first = t0 + k;
-  }
+  const float xt = mine ? trow[t] : -__builtin_huge_valf();
+  const float xd = mine ? drow[t] : -__builtin_huge_valf();
+  const double p = (double)scaled_exp(xt, Mt, c_log2) * iZt;
+  const double q = bonus ? 0.0 : (double)scaled_exp(xd, Md, c_log2) * iZd;
+  const double w = mine ? (use_p ? p : (p > q ? p - q : 0.0)) : 0.0;
+  const double tincl = wave_inclusive_scan(w);
+  const bool hit = mine && !fallback && !rfall && rbase + tincl > target;
+  int first = hit ? t : 0x7fffffff;
+  int last = mine && w > 0.0 ? t : -1;
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) {
     first = min(first, __shfl_xor(first, x, 64));
@@ -428,7 +488,8 @@ int32_t sample_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
 
 size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab) {
   const size_t C = (size_t)sample_chunks(vocab), R = 2 * (size_t)gamma + 1;
-  return sizeof(double) * B * R * C + 2 * sizeof(double) * B * C + sizeof(double) * B * R +
+  return sizeof(double) * B * R * C + 2 * sizeof(double) * B * C +
+         2 * sizeof(double) * B * C * kThreads + sizeof(double) * B * R +
          sizeof(float) * B * R * C + sizeof(float) * B * R + sizeof(int) * B;
 }
 
