@@ -27,6 +27,13 @@ selection frequencies), a dense single-query decode over the same KV (the
 one-layer autoregressive step), the committed tokens per round E, and the
 speedup E * t_dense / t_round next to the byte model's E * bytes_dense /
 bytes_round. One JSON line per point.
+
+--fidelity measures what the sparse draft gives up: per budget, the share of
+each query head's dense attention probability that falls on the selected pages
+(1 minus the total-variation distance between the sparse, renormalised and the
+dense attention distributions), at draft step 0 and at the round's last step for
+both selection frequencies, next to the best possible k pages. The dense
+probabilities are computed in fp32 with torch as the measuring stick.
 """
 import argparse
 import json
@@ -54,6 +61,8 @@ def parse():
                    help="rough budget of oracle CPU work for the baseline")
     p.add_argument("--sweep", action="store_true",
                    help="speedup-condition sweep instead of the one-round measurement")
+    p.add_argument("--fidelity", action="store_true",
+                   help="dense attention mass the page selection keeps, per budget")
     return p.parse_args()
 
 
@@ -215,6 +224,8 @@ def main():
                  "(the S3R hot path shards by sequence, with no exchange between GPUs)")
     if args.sweep:
         return sweep(args)
+    if args.fidelity:
+        return fidelity(args)
 
     import torch
 
@@ -320,6 +331,87 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+FIDELITY_BUDGETS = (256, 512, 1024, 2048, 4096)
+
+
+def fidelity(args):
+    """Attention mass kept by the page selection against dense attention, per budget."""
+    import torch
+
+    import self_sparse_speculative_paged_amd as s3r
+    from s3r_inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = make_workload(args.config, device=dev, seed=0, with_logits=False)
+    cfg = wl.cfg
+    B, Hq, Hkv, D, P, gamma = (cfg[k] for k in ("B", "Hq", "Hkv", "D", "P", "gamma"))
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+
+    def page_mass(step):
+        """Dense attention probability per (sequence, kv head, q head of the group, page)."""
+        q = wl.draft_q(step)
+        out = []
+        for b in range(B):
+            L = int(wl.seq_lens[step][b])
+            n = -(-L // P)
+            idx = wl.page_table[b, :n].long()
+            K = wl.k_pool.index_select(0, idx).float().permute(1, 0, 2, 3).reshape(Hkv, n * P, D)
+            logits = torch.bmm(q[b].float().view(Hkv, G, D), K.transpose(1, 2).contiguous()) * scale
+            logits[:, :, L:] = -float("inf")
+            out.append(torch.softmax(logits, dim=-1).view(Hkv, G, n, P).sum(-1))  # [Hkv][G][n]
+        return out
+
+    def kept(masses, sel):
+        """Per (sequence, q head): probability on the selected pages."""
+        vals = []
+        for b, pm in enumerate(masses):
+            n = pm.shape[-1]
+            mask = torch.zeros((Hkv, n), device=dev)
+            s = sel[b].long()
+            ok = (s >= 0) & (s < n)
+            mask.scatter_(1, torch.where(ok, s, torch.zeros_like(s)), ok.float())
+            vals.append((pm * mask[:, None, :]).sum(-1).flatten())
+        return torch.cat(vals)
+
+    def best(masses, k):
+        vals = []
+        for pm in masses:
+            n = pm.shape[-1]
+            top = torch.topk(pm.sum(1), min(k, n), dim=-1).indices  # by the group's summed mass
+            mask = torch.zeros((Hkv, n), device=dev).scatter_(1, top, 1.0)
+            vals.append((pm * mask[:, None, :]).sum(-1).flatten())
+        return torch.cat(vals)
+
+    def stats(v):
+        return {"mean": round(float(v.mean()), 4), "p10": round(float(v.quantile(0.1)), 4),
+                "min": round(float(v.min()), 4)}
+
+    m0, mlast = page_mass(0), page_mass(gamma - 1)
+    kv = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[0], Hq)
+    bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=dev)
+    for budget in FIDELITY_BUDGETS:
+        k = budget // P
+        kv.set_seq_lens(wl.seq_lens[0])
+        s3r.page_bounds_update(kv, bounds)
+        sel0, _ = s3r.page_select(kv, bounds, wl.draft_q(0), budget, scale)
+        _, sel_round, _ = s3r.sparse_draft_round(kv, bounds, wl.draft_q(0), budget, gamma, scale)
+        kv.set_seq_lens(wl.seq_lens[gamma - 1])
+        s3r.page_bounds_update(kv, bounds)
+        sel_last, _ = s3r.page_select(kv, bounds, wl.draft_q(gamma - 1), budget, scale)
+        torch.cuda.synchronize()
+        print(json.dumps({
+            "fidelity": {"workload": f"{args.config}_layer", "budget_tokens": budget, "pages": k,
+                         "draft_step": 0},
+            "kept_mass": stats(kept(m0, sel0)), "best_k_pages": stats(best(m0, k)),
+            "last_step": {"draft_step": gamma - 1,
+                          "kept_mass_per_step_select": stats(kept(mlast, sel_last)),
+                          "kept_mass_select_once": stats(kept(mlast, sel_round)),
+                          "best_k_pages": stats(best(mlast, k))},
+        }), flush=True)
 
 
 SWEEP_CONTEXTS = (8192, 32768)
