@@ -452,3 +452,37 @@ def test_ragged_longest_first_matches_oracle():
     check_pages(i32(sel), i32(nsel), rsel, rn, rsc, budget // 16)
     ref = oracle.sparse_draft_attn(f64(q0), K, V, pt, L0, i32(sel), scale)
     _check_attn(d_out, ref, "bf16")
+
+
+def test_round_and_commit_edge_cases():
+    """Empty, one-token and page-boundary lengths through the once-per-round
+    selection (k = 2 pages, gamma = 3) and a 3-row KV commit."""
+    gamma, budget = 3, 32
+    wl = _make(_cfg("bf16", 128, 4, 2, gamma=gamma, budget=budget), [8, 8, 20, 20, 20, 40], seed=27)
+    seq = torch.tensor([0, 1, 15, 16, 17, 33], dtype=torch.int32, device=DEV)
+    kvc = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, seq, wl.cfg["Hq"])
+    bounds = torch.zeros((wl.k_pool.shape[0], 2, 2, 128), dtype=torch.bfloat16, device=DEV)
+    s3r.page_bounds_update(kvc, bounds)
+    q0 = wl.draft_q(0)
+    out, sel, nsel = s3r.sparse_draft_round(kvc, bounds, q0, budget, gamma, 0.1)
+    torch.cuda.synchronize()
+    K, V, pt, L = f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table), i32(seq)
+    rb = oracle.page_bounds(K, pt, L)
+    rsel, rn, _ = oracle.page_select_round(rb, f64(q0), pt, L, budget, gamma, 0.1)
+    assert np.array_equal(i32(sel), rsel) and np.array_equal(i32(nsel), rn), (i32(sel), rsel)
+    assert i32(sel)[0].tolist() == [[0, -1], [0, -1]]  # nothing yet: the round's first page
+    ref = oracle.sparse_draft_attn(f64(q0), K, V, pt, L, rsel, 0.1)
+    assert np.all(out[0].cpu().numpy() == 0)
+    _check_attn(out, ref, "bf16")
+    first = torch.clamp(seq - 1, min=0).contiguous()
+    committed = (first + torch.tensor([1, 0, 2, 3, 1, 2], dtype=torch.int32, device=DEV)).contiguous()
+    g = torch.Generator(device="cpu").manual_seed(28)
+    k_new = torch.randn((6, 3, 2, 128), generator=g).to(torch.bfloat16).to(DEV)
+    v_new = torch.randn((6, 3, 2, 128), generator=g).to(torch.bfloat16).to(DEV)
+    B0 = f64(bounds)
+    rK, rV, rB = oracle.kv_commit(K, V, pt, f64(k_new), f64(v_new), i32(first), i32(committed), B0)
+    kvc.set_seq_lens(committed)
+    s3r.kv_commit(kvc, k_new, v_new, first, bounds)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(wl.k_pool), rK) and np.array_equal(f64(wl.v_pool), rV)
+    assert np.array_equal(f64(bounds), rB)
