@@ -67,7 +67,12 @@ typedef struct {
   int32_t max_pages_per_seq; /* row length of page_table */
   int32_t total_pages_hint;  /* host: sum over sequences of their page count,
                                 or 0 if unknown (then B * max_pages_per_seq is
-                                assumed). Only sizes the split-KV partitioning. */
+                                assumed). It sizes the split-KV partitioning and,
+                                when below half of B * max_pages_per_seq (a
+                                ragged batch), has the attention calls take the
+                                sequences longest first, which adds B int32 of
+                                scheduling order to their workspace. Results do
+                                not depend on it beyond rounding. */
   s3r_dtype kv_dtype;        /* dtype of k_pool, v_pool, bounds and q */
   const void* k_pool;
   const void* v_pool;
