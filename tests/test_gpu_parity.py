@@ -183,7 +183,8 @@ def _sample_case(B, gamma, V, noise, seed, T=1.0):
 
 @pytest.mark.parametrize("B,gamma,V,noise,T", [
     (64, 4, 1024, 0.5, 1.0), (16, 6, 151936, 0.5, 1.0), (24, 8, 32000, 1.35, 1.0),
-    (32, 2, 5000, 3.0, 1.0), (8, 3, 4099, 0.7, 0.6), (40, 1, 100, 0.0, 1.0)])
+    (32, 2, 5000, 3.0, 1.0), (8, 3, 4099, 0.7, 0.6), (40, 1, 100, 0.0, 1.0),
+    (4, 16, 2001, 0.5, 1.0)])  # the longest draft the library takes
 def test_spec_sample_matches_oracle(B, gamma, V, noise, T):
     d, t, x = _sample_case(B, gamma, V, noise, seed=B + V, T=T)
     out, n = s3r.spec_sample(d.to(DEV), t.to(DEV), x.to(DEV).int(), T, seed=0, offset=7)
@@ -486,3 +487,34 @@ def test_round_and_commit_edge_cases():
     torch.cuda.synchronize()
     assert np.array_equal(f64(wl.k_pool), rK) and np.array_equal(f64(wl.v_pool), rV)
     assert np.array_equal(f64(bounds), rB)
+
+
+def test_select_at_the_page_limit():
+    """page_select and the draft step at the select kernel's 12288-page limit
+    (the draft step's fused paths stop at 8192 and hand over to the separate
+    kernels), and a table one page wider, refused before any launch."""
+    gamma, budget = 4, 256
+    ctx = 12288 * 16 - gamma  # the table holds ctx + gamma positions: 12288 pages
+    wl = _make(_cfg("bf16", 64, 2, 1, gamma=gamma, budget=budget), [ctx], seed=71)
+    assert wl.max_pages == 12288
+    kvc = _kv(wl, 0)
+    bounds = torch.empty((wl.k_pool.shape[0], 1, 2, 64), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(kvc, bounds)
+    q0 = wl.draft_q(0)
+    sel, nsel = s3r.page_select(kvc, bounds, q0, budget, 0.125)
+    out, sel2, nsel2 = s3r.sparse_draft_step(kvc, bounds, q0, budget, 0.125,
+                                            refresh_from=(wl.seq_lens[0] - 1).contiguous())
+    torch.cuda.synchronize()
+    K, V, pt, L = f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table), i32(wl.seq_lens[0])
+    rb = oracle.page_bounds(K, pt, L)
+    rsel, rn, rsc = oracle.page_select(rb, f64(q0), pt, L, budget, 0.125)
+    check_pages(i32(sel), i32(nsel), rsel, rn, rsc, budget // 16)
+    assert torch.equal(sel, sel2) and torch.equal(nsel, nsel2)
+    ref = oracle.sparse_draft_attn(f64(q0), K, V, pt, L, i32(sel2), 0.125)
+    _check_attn(out, ref, "bf16")
+    wide = torch.zeros((1, 12289), dtype=torch.int32, device=DEV)
+    big = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wide, wl.seq_lens[0], wl.cfg["Hq"])
+    with pytest.raises(s3r.S3RError):
+        s3r.page_select(big, bounds, q0, budget, 0.125)
+    with pytest.raises(s3r.S3RError):
+        s3r.sparse_draft_step(big, bounds, q0, budget, 0.125)
