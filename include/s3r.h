@@ -35,7 +35,10 @@
  *   seq_lens   [B] int32                    KV positions visible to the last query
  *   bounds     [num_phys_pages][Hkv][2][D]  kv dtype; [0] elementwise key min,
  *                                           [1] elementwise key max of the page
- * Every physical page belongs to one sequence. A sequence with seq_len <= 0,
+ * Every physical page belongs to one sequence. The entries of a sequence's
+ * pages below seq_len must be valid physical pages (0 <= entry < num_phys_pages):
+ * attention, bounds and selection read them unchecked. Only the KV commit
+ * accepts a negative entry, as an unallocated page. A sequence with seq_len <= 0,
  * and a causal verify row that sees no position, get an all-zero output.
  */
 #ifndef S3R_H
@@ -201,7 +204,8 @@ s3r_status s3r_sparse_draft_round(const s3r_paged_kv* kv, void* bounds, const in
  *   k_new, v_new  [B][count][Hkv][D] kv dtype, 16-byte aligned: row i of
  *               sequence b goes to position first_pos[b] + i (logical page
  *               pos / P via page_table, slot pos % P; V transposed inside the
- *               page). Rows past max_pages_per_seq pages are dropped.
+ *               page). Rows past max_pages_per_seq pages, or in a page
+ *               whose page_table entry is negative (unallocated), are dropped.
  *   first_pos   [B] int32, >= 0.
  *   count       rows per sequence, >= 0 (0: a pure rollback).
  *   bounds      in/out [num_phys_pages][Hkv][2][D] kv dtype, or NULL for no

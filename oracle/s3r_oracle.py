@@ -122,7 +122,8 @@ def page_bounds(k_pool, page_table, seq_lens, seqs=None):
     """bounds[phys][h][0|1][d] = min|max over the page's valid tokens of K[t][h][d].
 
     Valid tokens of logical page j of sequence b: j*P <= t < min((j+1)*P, seq_len).
-    Physical pages not reached by any (b, j) are left as NaN.
+    Physical pages not reached by any (b, j) are left as NaN; a negative table
+    entry marks an unallocated page and is skipped.
     """
     n_phys, hkv, P, D = k_pool.shape
     out = np.full((n_phys, hkv, 2, D), np.nan)
@@ -131,6 +132,8 @@ def page_bounds(k_pool, page_table, seq_lens, seqs=None):
         L = int(seq_lens[b])
         for j in range(n_pages(L, P)):
             phys = page_table[b, j]
+            if phys < 0:
+                continue
             for h in range(hkv):
                 rows = np.stack([key_row(k_pool, page_table, b, h, t)
                                  for t in range(j * P, min((j + 1) * P, L))])
@@ -148,7 +151,8 @@ def kv_commit(k_pool, v_pool, page_table, k_new, v_new, first_pos, seq_lens, bou
     sequence's length is set back to what was committed. Row i of sequence b
     (k_new[b, i], v_new[b, i]: [Hkv][D]) goes to position first_pos[b] + i:
     logical page pos // P, slot pos % P, V transposed inside the page; rows
-    past the page table are dropped. seq_lens[b] is the committed length after
+    past the page table, or in a page whose table entry is negative (not
+    allocated), are dropped. seq_lens[b] is the committed length after
     the call; it may end inside the rows just written (a rollback: those rows
     stay in the pool but no longer count). Every logical page from
     min(first_pos[b], seq_lens[b] - 1) // P through the last page written or
@@ -166,7 +170,7 @@ def kv_commit(k_pool, v_pool, page_table, k_new, v_new, first_pos, seq_lens, bou
         f = int(first_pos[b])
         for i in range(count):
             pos = f + i
-            if pos // P >= max_pages:
+            if pos // P >= max_pages or page_table[b, pos // P] < 0:
                 continue
             phys = page_table[b, pos // P]
             K[phys, :, pos % P, :] = k_new[b, i]
@@ -177,7 +181,7 @@ def kv_commit(k_pool, v_pool, page_table, k_new, v_new, first_pos, seq_lens, bou
         lo = min(f, max(L - 1, 0)) // P
         hi = max((f + count - 1) // P if count > 0 else -1, n_pages(L, P) - 1)
         for j in range(lo, min(hi, max_pages - 1) + 1):
-            if j < n_pages(L, P):
+            if j < n_pages(L, P) and page_table[b, j] >= 0:
                 Bd[page_table[b, j]] = fresh[page_table[b, j]]
     return K, V, Bd
 

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(64) void kv_commit_kernel(KvCommitArgs a) {
   T* vp = static_cast<T*>(a.v_pool);
   for (int j = max(lo, 0) + blockIdx.y; j <= hi; j += gridDim.y) {
     const int phys = a.page_table[(size_t)b * a.max_pages + j];
+    if (phys < 0) continue;  // an unallocated page: its rows are dropped
     const int valid = min(kPage, L - kPage * j);  // tokens of this page below L (may be <= 0)
     T* kpage = kp + ((size_t)phys * a.Hkv + h) * kPage * kD;
     T* vpage = vp + ((size_t)phys * a.Hkv + h) * kD * kPage;

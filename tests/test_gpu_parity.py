@@ -518,3 +518,24 @@ def test_select_at_the_page_limit():
         s3r.page_select(big, bounds, q0, budget, 0.125)
     with pytest.raises(s3r.S3RError):
         s3r.sparse_draft_step(big, bounds, q0, budget, 0.125)
+
+
+def test_kv_commit_skips_unallocated_pages():
+    """Rows aimed at a page whose table entry is -1 are dropped on both sides."""
+    wl = _make(_cfg("bf16", 64, 2, 2, gamma=6), [30, 45], seed=53)
+    pt = wl.page_table.clone()
+    pt[0, 2] = -1
+    pt[1, 3] = -1
+    bounds = torch.zeros((wl.k_pool.shape[0], 2, 2, 64), dtype=torch.bfloat16, device=DEV)
+    first = (wl.seq_lens[0] - 1).contiguous()
+    committed = (first + 4).contiguous()
+    g = torch.Generator(device="cpu").manual_seed(54)
+    k_new = torch.randn((2, 5, 2, 64), generator=g).to(torch.bfloat16).to(DEV)
+    v_new = torch.randn((2, 5, 2, 64), generator=g).to(torch.bfloat16).to(DEV)
+    rK, rV, rB = oracle.kv_commit(f64(wl.k_pool), f64(wl.v_pool), i32(pt), f64(k_new), f64(v_new),
+                                  i32(first), i32(committed), f64(bounds))
+    kvc = s3r.PagedKVCache(wl.k_pool, wl.v_pool, pt, committed, wl.cfg["Hq"])
+    s3r.kv_commit(kvc, k_new, v_new, first, bounds)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(wl.k_pool), rK) and np.array_equal(f64(wl.v_pool), rV)
+    assert np.array_equal(f64(bounds), rB)

@@ -8,7 +8,8 @@
   nothing;
 * pages outside the touched range keep their bounds;
 * appending rows one at a time equals appending them at once;
-* rows past the page table are dropped;
+* rows past the page table, or in a page whose table entry is negative
+  (unallocated), are dropped;
 * a pure rollback (no rows) shrinks the tail page's bounds to its remaining
   tokens.
 """
@@ -118,3 +119,15 @@ def test_pure_rollback_shrinks_the_tail_page():
     assert np.array_equal(b2[pt[0, 2], 0, 0], rows.min(axis=0))
     assert np.array_equal(b2[pt[0, 2], 0, 1], rows.max(axis=0))
     assert np.array_equal(b2[pt[0, 0]], bounds[pt[0, 0]])
+
+
+def test_rows_in_an_unallocated_page_are_dropped():
+    wl, K, V, pt, L0, bounds = _setup(11, (30,), gamma=6)   # pages 0, 1 and 2 (positions < 36)
+    pt = pt.copy()
+    pt[0, 2] = -1                                            # page 2 not allocated
+    kn, vn = _new_rows(12, 1, 5, 2, 64)
+    K2, V2, B2 = oracle.kv_commit(K, V, pt, kn, vn, np.array([29]), np.array([33]), bounds)
+    for i in range(3):                                       # positions 29..31 land in page 1
+        assert np.array_equal(oracle.key_row(K2, pt, 0, 0, 29 + i), kn[0, i, 0])
+    untouched = [p for p in range(K.shape[0]) if p not in (pt[0, 0], pt[0, 1])]
+    assert np.array_equal(K2[untouched], K[untouched]) and np.array_equal(V2[untouched], V[untouched])
