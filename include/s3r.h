@@ -40,6 +40,24 @@
  * attention, bounds and selection read them unchecked. Only the KV commit
  * accepts a negative entry, as an unallocated page. A sequence with seq_len <= 0,
  * and a causal verify row that sees no position, get an all-zero output.
+ *
+ * Device data checks (S3R_DEBUG)
+ * ------------------------------
+ * The kernels trust three kinds of device data, which sit on the device and are
+ * not checked by default:
+ *   - seq_lens: ceil(seq_len / P) must not exceed max_pages_per_seq;
+ *   - page_table entries of the pages a call reads: each must lie in
+ *     [0, num_phys_pages), or be >= 0 when num_phys_pages is 0;
+ *   - draft_tokens of s3r_spec_sample: each must lie in [0, vocab).
+ * Selection lists, first_pos and refresh_from need no check: the kernels mask
+ * or clamp every value.
+ * When the environment variable S3R_DEBUG is set to anything but "" or "0" at
+ * call time, every call that reads such data first waits for its stream,
+ * copies that data to the host and checks it. On a bad value it prints the
+ * call, the index and the value to stderr and returns INVALID_ARGUMENT without
+ * launching anything. Such a call synchronises its stream, so it cannot be
+ * captured into a graph: under capture it returns UNSUPPORTED. A failed copy
+ * returns HIP.
  */
 #ifndef S3R_H
 #define S3R_H
@@ -81,6 +99,8 @@ typedef struct {
   const void* v_pool;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  int32_t num_phys_pages;    /* pages in k_pool, v_pool and bounds, or 0 if not
+                                given. Only the S3R_DEBUG checks read it. */
 } s3r_paged_kv;
 
 /* Workspace sizes in bytes (host computation only; 0 means none needed). */

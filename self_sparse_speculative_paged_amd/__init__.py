@@ -88,7 +88,8 @@ class PagedKVCache:
         self.struct = PagedKV(
             self.B, self.num_q_heads, self.Hkv, self.D, self.P, self.max_pages,
             self.total_pages_hint, _KV_DTYPES[self.dtype], self.k_pool.data_ptr(),
-            self.v_pool.data_ptr(), self.page_table.data_ptr(), seq_lens.data_ptr())
+            self.v_pool.data_ptr(), self.page_table.data_ptr(), seq_lens.data_ptr(),
+            self.k_pool.shape[0])
         return self
 
     def ref(self):

@@ -41,6 +41,7 @@ class PagedKV(ctypes.Structure):
         ("v_pool", ctypes.c_void_p),
         ("page_table", ctypes.c_void_p),
         ("seq_lens", ctypes.c_void_p),
+        ("num_phys_pages", ctypes.c_int32),
     ]
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libs3r.so")
 REPORT = os.path.join(PKG, "kernel_resources.txt")
-SOURCES = ["s3r_api.cpp", "s3r_attn.hip", "s3r_select.hip", "s3r_sample.hip", "s3r_kv.hip"]
+SOURCES = ["s3r_api.cpp", "s3r_debug.cpp", "s3r_attn.hip", "s3r_select.hip", "s3r_sample.hip", "s3r_kv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -10,14 +10,14 @@
 
 namespace {
 
-constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kVersion = 200;  // 0.2.0: s3r_paged_kv gained num_phys_pages
 constexpr int32_t kMaxRows = 64;   // G * n_queries per kv head (4 MFMA row blocks)
 constexpr int32_t kMaxGamma = 16;
 
 s3r_status check_kv(const s3r_paged_kv* kv) {
   if (kv == nullptr) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->num_seqs < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1 ||
-      kv->total_pages_hint < 0)
+      kv->total_pages_hint < 0 || kv->num_phys_pages < 0)
     return S3R_ERR_INVALID_ARGUMENT;
   if (kv->num_q_heads % kv->num_kv_heads != 0) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->page_table == nullptr || kv->seq_lens == nullptr)
@@ -36,6 +36,12 @@ s3r_status check_workspace(void* ws, size_t have, size_t need) {
 }
 
 s3r_status from_hip(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
+
+// Under S3R_DEBUG: the device data a call on kv would read, checked on the host.
+s3r_status debug_kv(const s3r_paged_kv& kv, void* stream, const char* where) {
+  if (!s3r::debug_checks_on()) return S3R_OK;
+  return s3r::debug_check_kv(kv, static_cast<hipStream_t>(stream), where);
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -62,11 +68,12 @@ s3r_status check_attention(const s3r_paged_kv* kv, const void* q, int32_t n_q, f
 
 s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* sel, int32_t ksel,
                          int32_t n_q, float scale, s3r_dtype out_dtype, void* out, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, void* stream, const char* where) {
   if (s3r_status s = check_attention(kv, q, n_q, scale, out_dtype, out)) return s;
   const int32_t max_items = sel ? ksel : kv->max_pages_per_seq;
   const s3r::SplitPlan plan = s3r::plan_attention(*kv, n_q, max_items);
   if (s3r_status s = check_workspace(ws, ws_bytes, attn_call_workspace(*kv, plan))) return s;
+  if (s3r_status s = debug_kv(*kv, stream, where)) return s;
   s3r::AttnArgs a = attn_args(kv, plan, q, sel, ksel, n_q, scale, out_dtype, out, ws);
   if (s3r::order_bytes(*kv))
     a.order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align256(plan.workspace_bytes));
@@ -269,6 +276,7 @@ s3r_status s3r_page_bounds_update(const s3r_paged_kv* kv, void* bounds, const in
                                                                   : kv->max_pages_per_seq)
                      : kv->max_pages_per_seq;
   a.pages_y = a.span;
+  if (s3r_status s = debug_kv(*kv, stream, "s3r_page_bounds_update")) return s;
   return from_hip(s3r::launch_bounds(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -283,6 +291,7 @@ s3r_status s3r_page_select(const s3r_paged_kv* kv, const void* bounds, const voi
   if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::select_workspace_bytes(kv->num_seqs, kv->num_kv_heads, kv->max_pages_per_seq);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  if (s3r_status s = debug_kv(*kv, stream, "s3r_page_select")) return s;
   const s3r::SelectArgs a = select_args(kv, bounds, q, budget_tokens, softmax_scale, selected,
                                         num_selected, workspace);
   return from_hip(s3r::launch_select(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
@@ -293,7 +302,7 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const in
                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (selected == nullptr || k < 1) return S3R_ERR_INVALID_ARGUMENT;
   return run_attention(kv, q, selected, k, 1, softmax_scale, out_dtype, out, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, "s3r_sparse_draft_attn");
 }
 
 size_t s3r_sparse_draft_step_workspace(const s3r_paged_kv* kv, int32_t budget_tokens) {
@@ -318,6 +327,8 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
   if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
   const DraftStepPlan plan = plan_draft_step(*kv, budget_tokens);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, plan.workspace_bytes)) return s;
+  if (s3r_status s = debug_kv(*kv, stream, round_gamma ? "s3r_sparse_draft_round" : "s3r_sparse_draft_step"))
+    return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t k = budget_tokens / kv->page_size;
   int32_t* order = s3r::order_bytes(*kv)
@@ -427,6 +438,10 @@ s3r_status s3r_kv_commit(const s3r_paged_kv* kv, const void* k_new, const void* 
   a.D = kv->head_dim;
   a.max_pages = kv->max_pages_per_seq;
   a.count = count;
+  if (s3r::debug_checks_on())
+    if (s3r_status s = s3r::debug_check_commit(*kv, first_pos, count, static_cast<hipStream_t>(stream),
+                                                "s3r_kv_commit"))
+      return s;
   return from_hip(s3r::launch_kv_commit(a, kv->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -434,7 +449,7 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t 
                                  float softmax_scale, s3r_dtype out_dtype, void* out,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   return run_attention(kv, q, nullptr, 0, n_q, softmax_scale, out_dtype, out, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, "s3r_dense_verify_attn");
 }
 
 s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
@@ -449,6 +464,10 @@ s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
     return S3R_ERR_INVALID_ARGUMENT;
   const size_t need = s3r::sample_workspace_bytes(num_seqs, gamma, vocab);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  if (s3r::debug_checks_on())
+    if (s3r_status s = s3r::debug_check_tokens(draft_tokens, num_seqs, gamma, vocab,
+                                                static_cast<hipStream_t>(stream), "s3r_spec_sample"))
+      return s;
   s3r::SampleArgs a{};
   a.draft_logits = draft_logits;
   a.target_logits = target_logits;

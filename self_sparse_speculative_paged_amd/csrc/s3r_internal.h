@@ -165,4 +165,17 @@ int32_t sample_chunks(int32_t vocab);
 size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 
+// Checks of the device data the kernels trust, run when S3R_DEBUG is set
+// (s3r_debug.cpp). Each waits for the stream and returns INVALID_ARGUMENT on a
+// value a launch would read out of range, UNSUPPORTED under graph capture.
+bool debug_checks_on();
+// seq_lens fit a page-table row and the entries below them name pool pages.
+s3r_status debug_check_kv(const s3r_paged_kv& kv, hipStream_t st, const char* where);
+// The entries a KV commit reads are below num_phys_pages (negative: unallocated).
+s3r_status debug_check_commit(const s3r_paged_kv& kv, const int32_t* first_pos, int32_t count,
+                              hipStream_t st, const char* where);
+// Draft token ids lie in [0, vocab).
+s3r_status debug_check_tokens(const int32_t* tokens, int32_t num_seqs, int32_t gamma, int32_t vocab,
+                              hipStream_t st, const char* where);
+
 }  // namespace s3r

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.s3r_version() == 100
+    assert lib.s3r_version() == 200
     assert lib.s3r_status_string(3) == b"S3R_ERR_WORKSPACE_TOO_SMALL"
     assert lib.s3r_status_string(99) == b"S3R_ERR_UNKNOWN"
 
@@ -37,14 +37,15 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 def _kv(**kw):
     f = dict(num_seqs=2, num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
              max_pages_per_seq=8, total_pages_hint=0, kv_dtype=_lib.S3R_BF16,
-             k_pool=FAKE, v_pool=FAKE, page_table=FAKE, seq_lens=FAKE)
+             k_pool=FAKE, v_pool=FAKE, page_table=FAKE, seq_lens=FAKE, num_phys_pages=0)
     f.update(kw)
     return _lib.PagedKV(**f)
 
 
 BAD_KV = [
     (dict(num_seqs=0), 1), (dict(num_q_heads=3), 1), (dict(num_kv_heads=0), 1),
-    (dict(max_pages_per_seq=0), 1), (dict(total_pages_hint=-1), 1), (dict(k_pool=None), 1),
+    (dict(max_pages_per_seq=0), 1), (dict(total_pages_hint=-1), 1), (dict(num_phys_pages=-1), 1),
+    (dict(k_pool=None), 1),
     (dict(v_pool=None), 1), (dict(page_table=None), 1), (dict(seq_lens=None), 1),
     (dict(head_dim=96), 2), (dict(page_size=32), 2), (dict(kv_dtype=7), 2),
     (dict(num_q_heads=18, num_kv_heads=2), 2),
