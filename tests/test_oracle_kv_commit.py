@@ -11,7 +11,8 @@
 * rows past the page table, or in a page whose table entry is negative
   (unallocated), are dropped;
 * a pure rollback (no rows) shrinks the tail page's bounds to its remaining
-  tokens.
+  tokens, and a rollback below the page the rows went to re-bounds the new
+  tail page.
 """
 import numpy as np
 import pytest
@@ -127,7 +128,23 @@ def test_rows_in_an_unallocated_page_are_dropped():
     pt[0, 2] = -1                                            # page 2 not allocated
     kn, vn = _new_rows(12, 1, 5, 2, 64)
     K2, V2, B2 = oracle.kv_commit(K, V, pt, kn, vn, np.array([29]), np.array([33]), bounds)
-    for i in range(3):                                       # positions 29..31 land in page 1
-        assert np.array_equal(oracle.key_row(K2, pt, 0, 0, 29 + i), kn[0, i, 0])
-    untouched = [p for p in range(K.shape[0]) if p not in (pt[0, 0], pt[0, 1])]
-    assert np.array_equal(K2[untouched], K[untouched]) and np.array_equal(V2[untouched], V[untouched])
+    # Positions 29..31 land in page 1; nothing else anywhere in either pool changes.
+    Ke, Ve = K.copy(), V.copy()
+    for i in range(3):
+        Ke[pt[0, 1], :, 13 + i, :] = kn[0, i]
+        Ve[pt[0, 1], :, :, 13 + i] = vn[0, i]
+    assert np.array_equal(K2, Ke) and np.array_equal(V2, Ve)
+
+
+def test_rollback_across_a_page_boundary_rebounds_the_new_tail_page():
+    # 45 tokens, three rows written at 44..46, then only 30 kept: the new tail
+    # is page 1 (tokens 16..29), below the page the rows went to.
+    wl, K, V, pt, L0, bounds = _setup(13, (45,))
+    kn, vn = _new_rows(14, 1, 3, 2, 64)
+    K2, _, b2 = oracle.kv_commit(K, V, pt, kn, vn, np.array([44]), np.array([30]), bounds)
+    for h in range(2):
+        rows = np.stack([oracle.key_row(K2, pt, 0, h, t) for t in range(16, 30)])
+        assert np.array_equal(b2[pt[0, 1], h, 0], rows.min(axis=0))
+        assert np.array_equal(b2[pt[0, 1], h, 1], rows.max(axis=0))
+    assert np.array_equal(b2[pt[0, 2]], bounds[pt[0, 2]])   # no valid token left: kept
+    assert np.array_equal(b2[pt[0, 0]], bounds[pt[0, 0]])
