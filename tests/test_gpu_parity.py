@@ -63,6 +63,11 @@ VERIFY_CASES = [
     ("bf16", 64, 8, 1, 7, (400, 95)),            # 64 rows: four row blocks, D=64
     ("bf16", 128, 8, 1, 7, (300, 77)),           # 64 rows at D=128: the one-stage pipeline
     ("bf16", 64, 2, 3, 3, (48, 2049)),
+    # query groups that are not a power of two
+    ("bf16", 128, 3, 2, 5, (500, 90)),           # 18 rows: two row blocks
+    ("bf16", 64, 5, 2, 2, (300, 33)),            # 15 rows: one row block
+    ("bf16", 128, 7, 1, 8, (260, 40)),           # 63 rows: four row blocks
+    ("f32", 128, 6, 1, 3, (200, 17)),            # 24 rows, fp32
 ]
 
 
@@ -109,6 +114,9 @@ SELECT_CASES = [
     ("bf16", 128, 2, 2, 160, (2000, 161)),
     ("f32", 64, 2, 2, 64, (512, 513)),
     ("bf16", 64, 8, 1, 32, (999, 1, 16)),
+    ("bf16", 128, 3, 2, 64, (700, 31)),
+    ("bf16", 64, 7, 1, 48, (400, 200)),
+    ("f32", 64, 5, 1, 32, (300, 64)),
 ]
 
 
@@ -133,6 +141,8 @@ DRAFT_CASES = [
     ("bf16", 128, 2, 2, 1024, (3000, 100)),     # many selected pages: several splits
     ("f32", 64, 2, 2, 64, (512, 300)),
     ("bf16", 64, 8, 1, 48, (333, 15)),
+    ("bf16", 128, 6, 1, 64, (500, 77)),
+    ("bf16", 64, 3, 2, 96, (650, 20)),
 ]
 
 
@@ -299,6 +309,11 @@ FUSED_CASES = [
     ("bf16", 64, 8, 8, 256, tuple(3000 - 90 * i for i in range(32))),
     ("bf16", 128, 1, 8, 2048, tuple(2100 + 61 * i for i in range(32))),
     ("f32", 64, 2, 2, 64, (512, 300)),         # fp32: the separate kernels
+    # groups that are not a power of two take the score kernel + attention
+    ("bf16", 128, 3, 2, 64, (700, 300)),
+    ("bf16", 64, 5, 2, 48, (1000, 20)),
+    ("bf16", 128, 6, 8, 512, tuple(60 + 97 * i for i in range(32))),  # fills the device
+    ("bf16", 64, 7, 1, 64, (9000, 150)),
 ]
 
 
@@ -363,6 +378,8 @@ ROUND_CASES = [
     ("f32", 64, 2, 2, 64, 3, (512, 300, 64)),         # fp32: the separate kernels
     ("bf16", 128, 4, 2, 64, 2, (9000, 200)),          # 563 pages, two kernels
     ("bf16", 64, 2, 1, 64, 5, (140000, 300)),         # 8750 pages: past the fused top-k
+    ("bf16", 128, 3, 2, 64, 4, (700, 300, 47)),       # G = 3: score kernel + attention
+    ("bf16", 64, 6, 8, 256, 6, tuple(90 + 61 * i for i in range(32))),  # G = 6, device-filling
 ]
 
 
