@@ -21,6 +21,8 @@
 // one 16-byte load. P is split into bf16 hi + lo parts so the P.V product keeps
 // ~16 mantissa bits. The fp32 path does the same on MFMA 16x16x4 f32, one page
 // per window.
+#include <climits>
+
 #include "s3r_common.h"
 #include "s3r_internal.h"
 #include "s3r_score.h"
@@ -618,22 +620,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Longest-first order: order[r] = the sequence of rank r by (length desc, index
 // asc). Thread b counts the sequences ranked before it over the lengths staged
-// in LDS, 1024 at a time.
+// in LDS, 1024 at a time, four per LDS read; slots past B hold INT_MIN, which
+// never ranks before a sequence (its index is past every b).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void order_by_length_kernel(const int32_t* seq_lens, int B,
                                                               int32_t* order) {
-  __shared__ int32_t lens[1024];
+  __shared__ int4 lens4[256];
+  int32_t* lens = reinterpret_cast<int32_t*>(lens4);
   const int b = blockIdx.x * 256 + threadIdx.x;
   const int L = b < B ? seq_lens[b] : 0;
   int rank = 0;
   for (int c0 = 0; c0 < B; c0 += 1024) {
     __syncthreads();
-    for (int c = threadIdx.x; c < 1024 && c0 + c < B; c += 256) lens[c] = seq_lens[c0 + c];
+    for (int c = threadIdx.x; c < 1024; c += 256) lens[c] = c0 + c < B ? seq_lens[c0 + c] : INT_MIN;
     __syncthreads();
-    const int n = min(1024, B - c0);
-    for (int c = 0; c < n; ++c) {
-      const int Lc = lens[c];
-      rank += (Lc > L) || (Lc == L && c0 + c < b);
+    const int n4 = (min(1024, B - c0) + 3) / 4;
+#pragma unroll 8
+    for (int c = 0; c < n4; ++c) {
+      const int4 v = lens4[c];
+      const int j = c0 + 4 * c;
+      rank += (v.x > L) | ((v.x == L) & (j < b));
+      rank += (v.y > L) | ((v.y == L) & (j + 1 < b));
+      rank += (v.z > L) | ((v.z == L) & (j + 2 < b));
+      rank += (v.w > L) | ((v.w == L) & (j + 3 < b));
     }
   }
   if (b < B) order[rank] = b;

@@ -472,6 +472,36 @@ def test_ragged_longest_first_matches_oracle():
     _check_attn(d_out, ref, "bf16")
 
 
+def test_longest_first_many_sequences_with_ties():
+    """1300 sequences (two 1024-length LDS passes of the ordering, six blocks),
+    most lengths shared, one long: every sequence must be taken exactly once.
+    Outputs start as NaN so a sequence the order skips cannot pass."""
+    rng = np.random.default_rng(71)
+    ctx = [int(x) for x in rng.choice([20, 33, 64, 150], size=1300)]
+    ctx[700] = 3000
+    gamma, budget = 2, 64
+    wl = _make(_cfg("bf16", 64, 2, 1, gamma=gamma, budget=budget), ctx, seed=71)
+    total = sum(-(-(L + gamma) // 16) for L in ctx)
+    assert wl.max_pages * len(ctx) > 2 * total
+    scale = 0.125
+    K, V, pt = f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table)
+    out = torch.full((len(ctx), gamma + 1, 2, 64), float("nan"), device=DEV)
+    s3r.dense_verify_attn(_kv(wl, gamma, hint=total), wl.q_verify, scale, out=out)
+    bounds = torch.empty((wl.k_pool.shape[0], 1, 2, 64), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(_kv(wl, 0), bounds)
+    q0 = wl.draft_q(0)
+    d_out = torch.full((len(ctx), 2, 64), float("nan"), device=DEV)
+    _, sel, nsel = s3r.sparse_draft_step(_kv(wl, 0, hint=total), bounds, q0, budget, scale,
+                                         refresh_from=(wl.seq_lens[0] - 1).contiguous(), out=d_out)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify_attn(f64(wl.q_verify), K, V, pt, i32(wl.seq_lens[gamma]), scale)
+    _check_attn(out, ref, "bf16")
+    L0 = i32(wl.seq_lens[0])
+    rsel, rn, rsc = oracle.page_select(oracle.page_bounds(K, pt, L0), f64(q0), pt, L0, budget, scale)
+    check_pages(i32(sel), i32(nsel), rsel, rn, rsc, budget // 16)
+    _check_attn(d_out, oracle.sparse_draft_attn(f64(q0), K, V, pt, L0, i32(sel), scale), "bf16")
+
+
 def test_round_and_commit_edge_cases():
     """Empty, one-token and page-boundary lengths through the once-per-round
     selection (k = 2 pages, gamma = 3) and a 3-row KV commit."""
