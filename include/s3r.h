@@ -17,12 +17,19 @@
  *   no device memory; scratch is the caller's `workspace`, sized by the
  *   matching *_workspace() query (host-only, no HIP call).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
- *   only enqueue work: no call synchronises the device or the host.
+ *   only enqueue work: no call synchronises the device or the host (except
+ *   under S3R_DEBUG).
  * - Host-side validation of scalars, pointers and shapes happens before any HIP
  *   call; a failed check returns its status and enqueues nothing. Device data
- *   (page ids, seq_lens, token ids) is trusted. No C++ exception crosses the
+ *   (page ids, seq_lens, token ids) is trusted unless S3R_DEBUG is set (see
+ *   "Device data checks" below). No C++ exception crosses the
  *   ABI. The library keeps no state between calls; calls on different streams
  *   are safe if their outputs and workspaces are disjoint.
+ * - k_pool, v_pool, bounds, q, attention outputs, new K/V rows and every
+ *   workspace must be 16-byte aligned (torch allocations are): the kernels
+ *   move them as 16-byte vectors. A misaligned one is INVALID_ARGUMENT.
+ *   Logits rows, page tables, lengths, selections and tokens need only their
+ *   element alignment.
  * - Supported: head_dim 64 or 128, page_size 16, num_q_heads a multiple of
  *   num_kv_heads with G = num_q_heads/num_kv_heads <= 8, kv dtype f32 or bf16,
  *   G * n_queries <= 64 attention rows per kv head, 1 <= gamma <= 16.

@@ -14,6 +14,10 @@ constexpr int32_t kVersion = 200;  // 0.2.0: s3r_paged_kv gained num_phys_pages
 constexpr int32_t kMaxRows = 64;   // G * n_queries per kv head (4 MFMA row blocks)
 constexpr int32_t kMaxGamma = 16;
 
+// The kernels move K/V rows, bounds, queries, outputs and workspace through
+// 16-byte vector accesses.
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 s3r_status check_kv(const s3r_paged_kv* kv) {
   if (kv == nullptr) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->num_seqs < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1 || kv->max_pages_per_seq < 1 ||
@@ -22,6 +26,7 @@ s3r_status check_kv(const s3r_paged_kv* kv) {
   if (kv->num_q_heads % kv->num_kv_heads != 0) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->k_pool == nullptr || kv->v_pool == nullptr || kv->page_table == nullptr || kv->seq_lens == nullptr)
     return S3R_ERR_INVALID_ARGUMENT;
+  if (misaligned(kv->k_pool) || misaligned(kv->v_pool)) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->kv_dtype != S3R_F32 && kv->kv_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
   if (kv->head_dim != 64 && kv->head_dim != 128) return S3R_ERR_UNSUPPORTED;
   if (kv->page_size != 16) return S3R_ERR_UNSUPPORTED;
@@ -31,7 +36,7 @@ s3r_status check_kv(const s3r_paged_kv* kv) {
 
 s3r_status check_workspace(void* ws, size_t have, size_t need) {
   if (have < need) return S3R_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && ws == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (need > 0 && (ws == nullptr || misaligned(ws))) return S3R_ERR_INVALID_ARGUMENT;
   return S3R_OK;
 }
 
@@ -60,6 +65,7 @@ s3r_status check_attention(const s3r_paged_kv* kv, const void* q, int32_t n_q, f
                            s3r_dtype out_dtype, void* out) {
   if (s3r_status s = check_kv(kv)) return s;
   if (q == nullptr || out == nullptr || n_q < 1 || !isfinite(scale)) return S3R_ERR_INVALID_ARGUMENT;
+  if (misaligned(q) || misaligned(out)) return S3R_ERR_INVALID_ARGUMENT;
   if (out_dtype != S3R_F32 && out_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
   const int32_t G = kv->num_q_heads / kv->num_kv_heads;
   if ((int64_t)G * n_q > kMaxRows) return S3R_ERR_UNSUPPORTED;
@@ -260,7 +266,7 @@ size_t s3r_spec_sample_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab)
 s3r_status s3r_page_bounds_update(const s3r_paged_kv* kv, void* bounds, const int32_t* first_pos,
                                   int32_t max_pages_touched, void* stream) {
   if (s3r_status s = check_kv(kv)) return s;
-  if (bounds == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (bounds == nullptr || misaligned(bounds)) return S3R_ERR_INVALID_ARGUMENT;
   if (first_pos != nullptr && max_pages_touched < 1) return S3R_ERR_INVALID_ARGUMENT;
   s3r::BoundsArgs a{};
   a.k_pool = kv->k_pool;
@@ -287,6 +293,7 @@ s3r_status s3r_page_select(const s3r_paged_kv* kv, const void* bounds, const voi
   if (s3r_status s = check_kv(kv)) return s;
   if (bounds == nullptr || q == nullptr || selected == nullptr || num_selected == nullptr)
     return S3R_ERR_INVALID_ARGUMENT;
+  if (misaligned(bounds) || misaligned(q)) return S3R_ERR_INVALID_ARGUMENT;
   if (budget_tokens < kv->page_size || !isfinite(softmax_scale)) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::select_workspace_bytes(kv->num_seqs, kv->num_kv_heads, kv->max_pages_per_seq);
@@ -322,7 +329,8 @@ s3r_status draft_step(const s3r_paged_kv* kv, void* bounds, const int32_t* refre
                       s3r_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes,
                       void* stream) {
   if (s3r_status s = check_attention(kv, q, 1, softmax_scale, out_dtype, out)) return s;
-  if (bounds == nullptr || selected == nullptr || num_selected == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (bounds == nullptr || selected == nullptr || num_selected == nullptr || misaligned(bounds))
+    return S3R_ERR_INVALID_ARGUMENT;
   if (budget_tokens < kv->page_size) return S3R_ERR_INVALID_ARGUMENT;
   if (kv->max_pages_per_seq > s3r::select_max_pages_supported()) return S3R_ERR_UNSUPPORTED;
   const DraftStepPlan plan = plan_draft_step(*kv, budget_tokens);
@@ -420,7 +428,7 @@ s3r_status s3r_kv_commit(const s3r_paged_kv* kv, const void* k_new, const void* 
   if (s3r_status s = check_kv(kv)) return s;
   if (first_pos == nullptr || count < 0) return S3R_ERR_INVALID_ARGUMENT;
   if (count > 0 && (k_new == nullptr || v_new == nullptr)) return S3R_ERR_INVALID_ARGUMENT;
-  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+  if (misaligned(k_new) || misaligned(v_new) || misaligned(bounds))
     return S3R_ERR_INVALID_ARGUMENT;  // rows are moved as 16-byte runs
   s3r::KvCommitArgs a{};
   a.k_new = k_new;

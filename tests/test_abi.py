@@ -147,3 +147,28 @@ def test_ragged_hint_reserves_the_longest_first_order():
     assert lib.s3r_attn_workspace(ragged, 5, maxp) >= lib.s3r_attn_workspace(even, 5, maxp) + order
     assert (lib.s3r_sparse_draft_step_workspace(ragged, 2048)
             >= lib.s3r_sparse_draft_step_workspace(even, 2048) + order)
+
+
+def test_misaligned_pointers_rejected():
+    """Every 16-byte vector operand is checked on the host (INVALID_ARGUMENT)."""
+    lib = _lib.load()
+    v = ctypes.c_void_p(FAKE)
+    m = ctypes.c_void_p(FAKE + 2)  # bf16-aligned, not 16-byte aligned
+    big = 1 << 30
+    kv = ctypes.byref(_kv())
+    for bad in (dict(k_pool=FAKE + 2), dict(v_pool=FAKE + 8)):
+        assert lib.s3r_dense_verify_attn(ctypes.byref(_kv(**bad)), v, 5, 0.1, 0, v, v, big, None) == 1
+    assert lib.s3r_page_bounds_update(kv, m, None, 1, None) == 1                       # bounds
+    assert lib.s3r_page_select(kv, m, v, 64, 0.1, v, v, v, big, None) == 1             # bounds
+    assert lib.s3r_page_select(kv, v, m, 64, 0.1, v, v, v, big, None) == 1             # q
+    assert lib.s3r_page_select(kv, v, v, 64, 0.1, v, v, m, big, None) == 1             # workspace
+    assert lib.s3r_sparse_draft_attn(kv, m, v, 4, 0.1, 0, v, v, big, None) == 1       # q
+    assert lib.s3r_sparse_draft_attn(kv, v, v, 4, 0.1, 0, m, v, big, None) == 1       # out
+    kv32 = ctypes.byref(_kv(kv_dtype=_lib.S3R_F32))  # fp32 partials go through the workspace
+    assert lib.s3r_attn_workspace(kv32, 5, 8) > 0
+    assert lib.s3r_dense_verify_attn(kv32, v, 5, 0.1, 0, v, m, big, None) == 1        # workspace
+    assert lib.s3r_sparse_draft_step(kv, m, None, v, 64, 0.1, v, v, 0, v, v, big, None) == 1  # bounds
+    assert lib.s3r_sparse_draft_round(kv, v, None, v, 64, 4, 0.1, v, v, 0, m, v, big, None) == 1  # out
+    assert lib.s3r_kv_commit(kv, v, m, v, 4, v, None) == 1                             # v_new
+    assert lib.s3r_kv_commit(kv, v, v, v, 4, m, None) == 1                             # bounds
+    assert lib.s3r_spec_sample(2, 4, 100, v, v, v, 1.0, 0, 0, v, v, m, big, None) == 1  # workspace
