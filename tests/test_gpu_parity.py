@@ -206,6 +206,34 @@ def test_spec_sample_matches_oracle(B, gamma, V, noise, T):
         assert np.all(i32(n) == gamma)
 
 
+@pytest.mark.parametrize("B,gamma,V,T", [(16, 4, 32000, 0.8), (8, 6, 151936, 1.0)])
+def test_spec_sample_masked_logits(B, gamma, V, T):
+    """Masked vocabularies (-inf logits): random masks in both distributions, so
+    many drafts have p(x) = 0, and a masked vocabulary tail that fills whole
+    4096-token chunks (their statistics are empty). Every emitted token must
+    have p > 0 at its slot, and the tokens follow the oracle."""
+    g = torch.Generator().manual_seed(V + B)
+    d = torch.randn((B, gamma, V), generator=g) * 2.0
+    t = torch.cat([d + torch.randn((B, gamma, V), generator=g) * 0.7,
+                   torch.randn((B, 1, V), generator=g) * 2.0], dim=1)
+    d[torch.rand(d.shape, generator=g) < 0.5] = float("-inf")
+    t[torch.rand(t.shape, generator=g) < 0.3] = float("-inf")
+    tail = V - V // 3
+    d[..., tail:] = float("-inf")
+    t[..., tail:] = float("-inf")
+    x = oracle.draw_draft_tokens(d.double().numpy(), T, seed=V, offset=0)
+    out, n = s3r.spec_sample(d.to(DEV), t.to(DEV), torch.from_numpy(x).to(DEV).int(), T, seed=3, offset=1)
+    torch.cuda.synchronize()
+    ro, rn, dec = oracle.spec_sample(d.double().numpy(), t.double().numpy(), x, T, 3, 1)
+    full = check_tokens(i32(out), i32(n), ro, rn, dec)
+    assert full >= B // 2, (full, B)
+    go, gn = i32(out), i32(n)
+    for b in range(B):
+        for i in range(gn[b] + 1):
+            assert np.isfinite(t[b, i, go[b, i]].item()), (b, i, go[b, i])
+    assert np.any(gn < gamma)  # the masks make rejections happen
+
+
 def test_determinism_bitwise():
     wl = _make(_cfg("bf16", 128, 4, 2, 6), [900, 300], seed=21)
     kvc = _kv(wl, 6)

@@ -48,9 +48,10 @@ def _enumerate(draft, target, T=1.0):
             nxt = []
             r = min(1.0, p[i][xs[i]] / q[i][xs[i]])
             for script, w in paths:
-                a = dict(script)
-                a[(i, 0)] = r / 2
-                nxt.append((a, w * r))
+                if r > 0.0:  # p(x) = 0 leaves no accept branch
+                    a = dict(script)
+                    a[(i, 0)] = r / 2
+                    nxt.append((a, w * r))
                 if r < 1.0:
                     res = np.maximum(0.0, p[i] - q[i])
                     for u, wu in intervals_icdf(res):
@@ -77,6 +78,28 @@ def test_exact_enumeration_vocab8(seed, gamma, T):
     rng = np.random.default_rng(seed)
     draft = rng.normal(0, 1.5, (gamma, 8))
     target = np.concatenate([draft + rng.normal(0, 0.8, (gamma, 8)), rng.normal(0, 1.5, (1, 8))])
+    _check_law(draft, target, T)
+
+
+def test_exact_enumeration_with_masked_tokens():
+    # -inf logits: tokens the drafter never proposes, tokens only the target
+    # rules out (their drafts are always rejected) and tokens masked in both.
+    rng = np.random.default_rng(7)
+    gamma = 2
+    draft = rng.normal(0, 1.5, (gamma, 8))
+    target = np.concatenate([draft + rng.normal(0, 0.8, (gamma, 8)), rng.normal(0, 1.5, (1, 8))])
+    draft[0, [1, 5]] = -np.inf
+    draft[1, [0, 7]] = -np.inf
+    target[0, [2, 5]] = -np.inf
+    target[1, [3]] = -np.inf
+    target[2, [6, 7]] = -np.inf
+    law = _check_law(draft, target, 1.0)
+    for (n, toks), w in law.items():  # no emitted token is impossible under its target
+        assert all(np.isfinite(target[j, t]) for j, t in enumerate(toks)) or w == 0.0
+
+
+def _check_law(draft, target, T):
+    gamma = draft.shape[0]
     law, p, q = _enumerate(draft, target, T)
     assert abs(sum(law.values()) - 1.0) < 1e-12
     alpha = [np.minimum(p[i], q[i]).sum() for i in range(gamma)]
@@ -93,6 +116,7 @@ def test_exact_enumeration_vocab8(seed, gamma, T):
     # joint law of the emitted prefix given acceptance of earlier positions
     for (n, toks), w in law.items():
         assert len(toks) == n + 1
+    return law
 
 
 def _mc_batch(V, gamma, B, noise, seed, q_equals_p=False):
