@@ -530,6 +530,30 @@ def test_longest_first_many_sequences_with_ties():
     _check_attn(d_out, oracle.sparse_draft_attn(f64(q0), K, V, pt, L0, i32(sel), scale), "bf16")
 
 
+@pytest.mark.parametrize("hint", [False, True], ids=["plain", "ragged_hint"])
+def test_very_long_context(hint):
+    """300K tokens (18753 pages) beside a 50-token sequence: verify over many
+    split groups and the global combine, and a sparse draft over 64 pages
+    spread across the whole context (past what the in-kernel top-k ranks)."""
+    ctx = [300000, 50]
+    gamma = 3
+    wl = _make(_cfg("bf16", 64, 2, 1, gamma=gamma, budget=1024), ctx, seed=81)
+    total = sum(-(-(L + gamma) // 16) for L in ctx) if hint else 0
+    K, V, pt = f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table)
+    out = s3r.dense_verify_attn(_kv(wl, gamma, hint=total), wl.q_verify, 0.125)
+    rng = np.random.default_rng(81)
+    sel = np.full((2, 1, 64), -1, dtype=np.int32)
+    sel[0, 0] = np.sort(rng.choice(18750, size=64, replace=False))
+    sel[1, 0, :4] = np.arange(4)
+    d_out = s3r.sparse_draft_attn(_kv(wl, 0, hint=total), wl.draft_q(0), torch.from_numpy(sel).to(DEV),
+                                  0.125)
+    torch.cuda.synchronize()
+    ref = oracle.dense_verify_attn(f64(wl.q_verify), K, V, pt, i32(wl.seq_lens[gamma]), 0.125)
+    _check_attn(out, ref, "bf16")
+    rd = oracle.sparse_draft_attn(f64(wl.draft_q(0)), K, V, pt, i32(wl.seq_lens[0]), sel, 0.125)
+    _check_attn(d_out, rd, "bf16")
+
+
 def test_round_and_commit_edge_cases():
     """Empty, one-token and page-boundary lengths through the once-per-round
     selection (k = 2 pages, gamma = 3) and a 3-row KV commit."""
