@@ -147,8 +147,8 @@ s3r_status s3r_page_bounds_update(const s3r_paged_kv* kv, void* bounds, const in
  *   selected     out [B][Hkv][k] int32 logical page ids, ascending, -1 padded.
  *   num_selected out [B] int32 = min(k, n).
  * Errors: INVALID_ARGUMENT for NULL pointers or budget_tokens < P;
- * UNSUPPORTED if max_pages_per_seq > 12288 (the block top-k holds at most
- * 12288 page keys per row); WORKSPACE_TOO_SMALL if workspace_bytes <
+ * UNSUPPORTED if max_pages_per_seq > 32768 (the block top-k holds at most
+ * 32768 page keys per row, 524288 tokens); WORKSPACE_TOO_SMALL if workspace_bytes <
  * s3r_page_select_workspace().
  * Scores are fp32; ties closer than fp32 rounding may order differently from an
  * exact computation.

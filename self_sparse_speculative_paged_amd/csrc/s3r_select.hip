@@ -21,7 +21,7 @@
 namespace s3r {
 namespace {
 
-constexpr int kMaxSelectPages = 12288;  // 12 keys per thread of the 1024-thread top-k block
+constexpr int kMaxSelectPages = 32768;  // 32 keys per thread of the 1024-thread top-k block
 constexpr int kSelectPagesPerBlock = 128;  // pages scored by one 256-thread block
 
 // ---------------------------------------------------------------------------

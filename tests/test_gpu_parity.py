@@ -589,13 +589,13 @@ def test_round_and_commit_edge_cases():
 
 
 def test_select_at_the_page_limit():
-    """page_select and the draft step at the select kernel's 12288-page limit
+    """page_select and the draft step at the select kernel's 32768-page limit
     (the draft step's fused paths stop at 8192 and hand over to the separate
     kernels), and a table one page wider, refused before any launch."""
     gamma, budget = 4, 256
-    ctx = 12288 * 16 - gamma  # the table holds ctx + gamma positions: 12288 pages
+    ctx = 32768 * 16 - gamma  # the table holds ctx + gamma positions: 32768 pages
     wl = _make(_cfg("bf16", 64, 2, 1, gamma=gamma, budget=budget), [ctx], seed=71)
-    assert wl.max_pages == 12288
+    assert wl.max_pages == 32768
     kvc = _kv(wl, 0)
     bounds = torch.empty((wl.k_pool.shape[0], 1, 2, 64), dtype=wl.k_pool.dtype, device=DEV)
     s3r.page_bounds_update(kvc, bounds)
@@ -611,7 +611,7 @@ def test_select_at_the_page_limit():
     assert torch.equal(sel, sel2) and torch.equal(nsel, nsel2)
     ref = oracle.sparse_draft_attn(f64(q0), K, V, pt, L, i32(sel2), 0.125)
     _check_attn(out, ref, "bf16")
-    wide = torch.zeros((1, 12289), dtype=torch.int32, device=DEV)
+    wide = torch.zeros((1, 32769), dtype=torch.int32, device=DEV)
     big = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wide, wl.seq_lens[0], wl.cfg["Hq"])
     with pytest.raises(s3r.S3RError):
         s3r.page_select(big, bounds, q0, budget, 0.125)
