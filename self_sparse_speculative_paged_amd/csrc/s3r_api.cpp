@@ -143,10 +143,9 @@ s3r::SelectArgs select_args(const s3r_paged_kv* kv, const void* bounds, const vo
   return a;
 }
 
-// Eight waves per (sequence, kv head), the selection split evenly over them:
+// kWaves waves per (sequence, kv head), the selection split evenly over them:
 // the draft's plan whenever its top-k runs inside the attention workgroup.
-s3r::SplitPlan eight_wave_plan(const s3r_paged_kv& kv, int32_t k) {
-  constexpr int kWaves = 8;
+s3r::SplitPlan wave_plan(const s3r_paged_kv& kv, int32_t k, int kWaves) {
   s3r::SplitPlan a{};
   const int32_t G = kv.num_q_heads / kv.num_kv_heads;
   a.rows = G;
@@ -164,7 +163,7 @@ s3r::SplitPlan eight_wave_plan(const s3r_paged_kv& kv, int32_t k) {
   return a;
 }
 
-// The fused draft step keeps the selection list in LDS after the per-wave
+// The two-kernel draft step keeps the selection list in LDS after the per-wave
 // regions; it needs bf16 KV, at most 64 KB of LDS and a page table short
 // enough for its in-register top-k. A selection that fits one workgroup runs
 // on eight waves, so the top-k has 512 threads.
@@ -182,7 +181,7 @@ DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
   const int32_t k = budget_tokens / kv.page_size;
   p.attn = s3r::plan_attention(kv, 1, k);
   if (kv.kv_dtype == S3R_BF16 && p.attn.row_blocks == 1 && p.attn.waves_per_group < 8)
-    p.attn = eight_wave_plan(kv, k);
+    p.attn = wave_plan(kv, k, 8);
   p.select_ws = s3r::select_workspace_bytes(kv.num_seqs, kv.num_kv_heads, kv.max_pages_per_seq);
   const int32_t w = p.attn.waves_per_group;
   const size_t regions = (size_t)p.attn.lds_region_bytes * w;
@@ -213,10 +212,10 @@ int32_t device_cu_count() {
   return v;
 }
 
-// Single-kernel draft step: one 8-wave workgroup per (sequence, kv head) that
-// scores, ranks and attends. It pays off when those workgroups fill the
-// device; each reads its whole bounds row, so it needs the row's page ids,
-// its scores and the list in LDS and its keys in the top-k's registers.
+// Single-kernel draft step: one workgroup of four or eight waves per (sequence,
+// kv head) that scores, ranks and attends. It pays off when those workgroups
+// fill the device; each reads its whole bounds row, so it needs the row's page
+// ids, its scores and the list in LDS and its keys in the top-k's registers.
 struct SingleKernelPlan {
   bool ok;
   s3r::SplitPlan attn;
@@ -224,13 +223,20 @@ struct SingleKernelPlan {
 };
 
 SingleKernelPlan plan_single_kernel(const s3r_paged_kv& kv, int32_t k) {
-  constexpr int kWaves = 8;
   SingleKernelPlan p{};
   const int32_t G = kv.num_q_heads / kv.num_kv_heads;
   if (kv.kv_dtype != S3R_BF16 || (G != 1 && G != 2 && G != 4 && G != 8)) return p;
+  const int64_t items = (int64_t)kv.num_seqs * kv.num_kv_heads;
+  const int32_t cus = device_cu_count();
+  if (items < cus) return p;
+  // Eight waves per workgroup give one resident workgroup per CU. With at
+  // least two (sequence, kv head) pairs per CU, workgroups of four waves let
+  // two share each CU at once, so one's ranking overlaps the other's reads.
+  // Their 256-thread top-k ranks at most 2048 pages.
+  const int kWaves =
+      items >= 2 * (int64_t)cus && kv.max_pages_per_seq <= s3r::fused_topk_keys(4) * 64 * 4 ? 4 : 8;
   if (kv.max_pages_per_seq > s3r::fused_topk_keys(kWaves) * 64 * kWaves) return p;
-  if ((int64_t)kv.num_seqs * kv.num_kv_heads < device_cu_count()) return p;
-  const s3r::SplitPlan& a = p.attn = eight_wave_plan(kv, k);
+  const s3r::SplitPlan& a = p.attn = wave_plan(kv, k, kWaves);
   const size_t row = sizeof(int32_t) * (size_t)kv.max_pages_per_seq;
   size_t front = (size_t)a.lds_region_bytes * kWaves;
   if (front < row) front = row;  // the scores alias the wave regions

@@ -738,20 +738,29 @@ hipError_t launch_typed(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The one-kernel draft step with kW waves per (sequence, kv head).
+template <int kD, int kW>
+hipError_t launch_score_here(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+  const dim3 block(64 * kW);
+  switch (a.G) {
+    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 1>), grid, block, lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 2>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 4>), grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 8>), grid, block, lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int kD>
 hipError_t launch_fused_draft(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_groups));
   const size_t lds = (size_t)a.list_offset + sizeof(int32_t) * a.ksel;
-  if (a.score_here) {  // one group of 8 waves per (sequence, kv head)
-    if (a.waves_per_group != 8 || a.n_groups != 1) return hipErrorInvalidValue;
-    switch (a.G) {
-      case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 1>), grid, dim3(512), lds, stream, a); break;
-      case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 2>), grid, dim3(512), lds, stream, a); break;
-      case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 4>), grid, dim3(512), lds, stream, a); break;
-      case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelScoreHere, 8>), grid, dim3(512), lds, stream, a); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+  if (a.score_here) {  // one group of 4 or 8 waves per (sequence, kv head)
+    if (a.n_groups != 1) return hipErrorInvalidValue;
+    if (a.waves_per_group == 4) return launch_score_here<kD, 4>(a, grid, lds, stream);
+    if (a.waves_per_group == 8) return launch_score_here<kD, 8>(a, grid, lds, stream);
+    return hipErrorInvalidValue;
   }
   switch (a.waves_per_group) {
     case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 1, kSelFromScores>), grid, dim3(64), lds, stream, a); break;

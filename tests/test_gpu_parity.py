@@ -342,6 +342,10 @@ FUSED_CASES = [
     ("bf16", 64, 5, 2, 48, (1000, 20)),
     ("bf16", 128, 6, 8, 512, tuple(60 + 97 * i for i in range(32))),  # fills the device
     ("bf16", 64, 7, 1, 64, (9000, 150)),
+    # 64 sequences x 8 kv heads: two (sequence, kv head) pairs per CU, so the
+    # single-kernel step runs four-wave workgroups, two per CU
+    ("bf16", 128, 2, 8, 256, tuple(50 + 37 * i for i in range(64))),
+    ("bf16", 64, 8, 8, 128, tuple(900 - 13 * i for i in range(64))),
 ]
 
 
@@ -408,6 +412,7 @@ ROUND_CASES = [
     ("bf16", 64, 2, 1, 64, 5, (140000, 300)),         # 8750 pages: past the fused top-k
     ("bf16", 128, 3, 2, 64, 4, (700, 300, 47)),       # G = 3: score kernel + attention
     ("bf16", 64, 6, 8, 256, 6, tuple(90 + 61 * i for i in range(32))),  # G = 6, device-filling
+    ("bf16", 128, 2, 8, 256, 4, tuple(40 + 29 * i for i in range(64))),  # four-wave single kernel
 ]
 
 
