@@ -232,10 +232,11 @@ SingleKernelPlan plan_single_kernel(const s3r_paged_kv& kv, int32_t k) {
   // Eight waves per workgroup give one resident workgroup per CU. With at
   // least two (sequence, kv head) pairs per CU, workgroups of four waves let
   // two share each CU at once, so one's ranking overlaps the other's reads.
-  // Their 256-thread top-k ranks at most 2048 pages.
+  // Their 256-thread top-k ranks up to kWideTopkKeys * 256 pages.
   const int kWaves =
-      items >= 2 * (int64_t)cus && kv.max_pages_per_seq <= s3r::fused_topk_keys(4) * 64 * 4 ? 4 : 8;
-  if (kv.max_pages_per_seq > s3r::fused_topk_keys(kWaves) * 64 * kWaves) return p;
+      items >= 2 * (int64_t)cus && kv.max_pages_per_seq <= s3r::kWideTopkKeys * 64 * 4 ? 4 : 8;
+  const int keys = kWaves == 4 ? s3r::kWideTopkKeys : s3r::fused_topk_keys(kWaves);
+  if (kv.max_pages_per_seq > keys * 64 * kWaves) return p;
   const s3r::SplitPlan& a = p.attn = wave_plan(kv, k, kWaves);
   const size_t row = sizeof(int32_t) * (size_t)kv.max_pages_per_seq;
   size_t front = (size_t)a.lds_region_bytes * kWaves;

@@ -341,7 +341,8 @@ __device__ __forceinline__ void score_row_to_lds(const AttnArgs& a, int b, int h
 // from this workgroup too (kG q heads per kv head, one group per (sequence,
 // kv head)): LDS then holds the scores over the wave regions (dead once the
 // top-k has read them), the page-table row at pt_offset and the list.
-template <int kD, int kNB, bool kSparse, int kW, int kSelect = kSelGiven, int kG = 0>
+template <int kD, int kNB, bool kSparse, int kW, int kSelect = kSelGiven, int kG = 0,
+          int kKeys = fused_topk_keys(kW)>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(bf16_waves_per_simd<kNB>(), 8)))
 void attn_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
@@ -383,7 +384,7 @@ void attn_bf16_kernel(AttnArgs a) {
       scores = sc;
       pt_row = pt_lds;
     }
-    select_pages<64 * kW, fused_topk_keys(kW)>(scores, n_pages, k, fut0, nfut, sh, list);
+    select_pages<64 * kW, kKeys>(scores, n_pages, k, fut0, nfut, sh, list);
     __syncthreads();
     if (group == 0) {
       int32_t* out = a.sel_out + (size_t)bh * k;
@@ -738,15 +739,16 @@ hipError_t launch_typed(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The one-kernel draft step with kW waves per (sequence, kv head).
-template <int kD, int kW>
+// The one-kernel draft step with kW waves per (sequence, kv head) and kKeys
+// page keys per thread in its top-k.
+template <int kD, int kW, int kKeys>
 hipError_t launch_score_here(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
   const dim3 block(64 * kW);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 1>), grid, block, lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 2>), grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 4>), grid, block, lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 8>), grid, block, lds, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 1, kKeys>), grid, block, lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 2, kKeys>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 4, kKeys>), grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, kW, kSelScoreHere, 8, kKeys>), grid, block, lds, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -758,8 +760,11 @@ hipError_t launch_fused_draft(const AttnArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)a.list_offset + sizeof(int32_t) * a.ksel;
   if (a.score_here) {  // one group of 4 or 8 waves per (sequence, kv head)
     if (a.n_groups != 1) return hipErrorInvalidValue;
-    if (a.waves_per_group == 4) return launch_score_here<kD, 4>(a, grid, lds, stream);
-    if (a.waves_per_group == 8) return launch_score_here<kD, 8>(a, grid, lds, stream);
+    if (a.waves_per_group == 4)
+      return a.max_pages <= fused_topk_keys(4) * 256
+                 ? launch_score_here<kD, 4, fused_topk_keys(4)>(a, grid, lds, stream)
+                 : launch_score_here<kD, 4, kWideTopkKeys>(a, grid, lds, stream);
+    if (a.waves_per_group == 8) return launch_score_here<kD, 8, fused_topk_keys(8)>(a, grid, lds, stream);
     return hipErrorInvalidValue;
   }
   switch (a.waves_per_group) {

@@ -148,6 +148,10 @@ int32_t select_max_pages_supported();
 // workgroup ranks at most fused_topk_keys(W) * 64 * W pages per sequence
 // (8192 at W = 8); longer page tables take the separate select kernel.
 constexpr int fused_topk_keys(int waves) { return waves >= 8 ? 16 : 8; }
+// The one-kernel step's four-wave workgroups also come with 32 keys per
+// thread (8192 pages), used only for tables past fused_topk_keys(4) * 256
+// pages: unused keys cost a uniform branch each, so short tables keep 8.
+constexpr int kWideTopkKeys = 32;
 
 struct SampleArgs {
   const float* draft_logits;
