@@ -797,7 +797,10 @@ hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
 SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items) {
   // As many splits as resident waves: 256 CUs x 4 SIMDs x (2 waves per SIMD
   // for one MFMA row block, 1 otherwise).
-  constexpr long kMinPagesPerSplit = 16;
+  // A single query (a draft step over a short selection) splits down to one
+  // two-page window per wave: its few pages then spread over a workgroup's
+  // waves instead of streaming through one. Multi-query splits keep 16 pages.
+  const long kMinPagesPerSplit = n_queries == 1 ? 2 : 16;
   constexpr long kMaxPagesPerSplit = 4096;   // LDS window table <= 32 KB
   constexpr size_t kMaxGroupLds = 64 * 1024;
   SplitPlan p{};
