@@ -7,9 +7,12 @@
 // pages are read (a selection row vs every page) and in the number of query
 // positions (1 vs gamma + 1, causally masked).
 //
-// One wave64 workgroup owns one (sequence, kv head, split) work item and all
-// rows = G * n_queries query rows of that kv head, so every K/V tile read from
-// HBM is used by the whole GQA group and all verify positions.
+// Each wave owns one split (a range of pages, or of selection entries) of one
+// (sequence, kv head) and computes all rows = G * n_queries query rows of that
+// kv head, so every K/V tile read from HBM serves the whole GQA group and all
+// verify positions. The W waves of a workgroup hold splits of the same
+// (sequence, kv head) and merge their partials in LDS; a combine kernel merges
+// the workgroups' partials when one (sequence, kv head) spans several.
 //
 // bf16 path, per window of two pages (32 tokens), on MFMA 16x16x32 bf16:
 //   S^T[token][row] = K[token][:] . Q[row][:]     A = K rows,  B = Q^T
