@@ -13,6 +13,8 @@ Entry points (same names as include/s3r.h without the prefix):
   roll back), dense_verify_attn, spec_sample, and the workspace queries.
 """
 import ctypes
+import functools
+import threading
 
 import torch
 
@@ -41,11 +43,37 @@ def _check(status, where):
         raise S3RError(status, where)
 
 
+_call = threading.local()  # the device of the entry-point call in progress on this thread
+
+
+def _on_device(fn):
+    """Runs an entry point with the device of its first argument (the KV cache,
+    or the draft logits) current: the library launches on the current device,
+    so every tensor of the call must live there, and the default stream is that
+    device's current stream."""
+    @functools.wraps(fn)
+    def call(first, *args, **kwargs):
+        dev = first.device
+        if dev.type != "cuda":
+            raise ValueError(f"{fn.__name__}: tensors must be on a GPU, got {dev}")
+        prev = getattr(_call, "device", None)
+        _call.device = dev
+        try:
+            with torch.cuda.device(dev):
+                return fn(first, *args, **kwargs)
+        finally:
+            _call.device = prev
+    return call
+
+
 def _dev(t, name, dtype=None, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    want = getattr(_call, "device", None)
+    if want is not None and t.device != want:
+        raise ValueError(f"{name} is on {t.device}; this call's tensors are on {want}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -57,6 +85,9 @@ def _dev(t, name, dtype=None, shape=None):
 
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
+    want = getattr(_call, "device", None)
+    if want is not None and s.device != want:
+        raise ValueError(f"stream is on {s.device}; this call's tensors are on {want}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -72,9 +103,13 @@ class PagedKVCache:
             raise ValueError(f"kv dtype must be float32 or bfloat16, got {k_pool.dtype}")
         n_phys, hkv, P, D = k_pool.shape
         _dev(k_pool, "k_pool")
+        self.device = k_pool.device
         _dev(v_pool, "v_pool", k_pool.dtype, (n_phys, hkv, D, P))
         B, maxp = page_table.shape
         _dev(page_table, "page_table", torch.int32)
+        for t, name in ((v_pool, "v_pool"), (page_table, "page_table")):
+            if t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, k_pool on {self.device}")
         self.k_pool, self.v_pool, self.page_table = k_pool, v_pool, page_table
         self.num_q_heads = num_q_heads
         self.total_pages_hint = int(total_pages_hint)
@@ -84,6 +119,8 @@ class PagedKVCache:
 
     def set_seq_lens(self, seq_lens):
         _dev(seq_lens, "seq_lens", torch.int32, (self.B,))
+        if seq_lens.device != self.device:
+            raise ValueError(f"seq_lens is on {seq_lens.device}, the pools on {self.device}")
         self.seq_lens = seq_lens
         self.struct = PagedKV(
             self.B, self.num_q_heads, self.Hkv, self.D, self.P, self.max_pages,
@@ -119,6 +156,7 @@ def _workspace(nbytes, like, workspace):
     return workspace
 
 
+@_on_device
 def page_bounds_update(kv, bounds, first_pos=None, max_pages_touched=1, stream=None):
     """Recompute the key min/max bounds of touched pages (all pages if first_pos is None)."""
     lib = _lib.load()
@@ -130,6 +168,7 @@ def page_bounds_update(kv, bounds, first_pos=None, max_pages_touched=1, stream=N
     return bounds
 
 
+@_on_device
 def page_select(kv, bounds, q, budget_tokens, scale, selected=None, num_selected=None,
                 workspace=None, stream=None):
     """Top-k pages per (sequence, kv head) by key-bound score; returns (selected, num_selected)."""
@@ -153,6 +192,7 @@ def page_select(kv, bounds, q, budget_tokens, scale, selected=None, num_selected
 _OUT_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
 
 
+@_on_device
 def sparse_draft_attn(kv, q, selected, scale, out=None, out_dtype=torch.float32,
                       workspace=None, stream=None):
     """One draft step's attention over the selected pages; returns out [B][Hq][D]."""
@@ -173,6 +213,7 @@ def sparse_draft_step_workspace(kv, budget_tokens):
     return _lib.load().s3r_sparse_draft_step_workspace(kv.ref(), budget_tokens)
 
 
+@_on_device
 def sparse_draft_step(kv, bounds, q, budget_tokens, scale, refresh_from=None, selected=None,
                       num_selected=None, out=None, out_dtype=torch.float32, workspace=None,
                       stream=None):
@@ -199,6 +240,7 @@ def sparse_draft_step(kv, bounds, q, budget_tokens, scale, refresh_from=None, se
     return out, selected, num_selected
 
 
+@_on_device
 def sparse_draft_round(kv, bounds, q, budget_tokens, gamma, scale, refresh_from=None,
                        selected=None, num_selected=None, out=None, out_dtype=torch.float32,
                        workspace=None, stream=None):
@@ -227,6 +269,7 @@ def sparse_draft_round(kv, bounds, q, budget_tokens, gamma, scale, refresh_from=
     return out, selected, num_selected
 
 
+@_on_device
 def kv_commit(kv, k_new, v_new, first_pos, bounds=None, stream=None):
     """Write k_new/v_new [B][count][Hkv][D] at positions first_pos[b] + i into the
     pools of kv and bring the touched pages' bounds up to date for kv's
@@ -243,6 +286,7 @@ def kv_commit(kv, k_new, v_new, first_pos, bounds=None, stream=None):
     return bounds
 
 
+@_on_device
 def dense_verify_attn(kv, q, scale, out=None, out_dtype=torch.float32, workspace=None,
                       stream=None):
     """Causal verify attention of q [B][n_q][Hq][D] over every page; returns out like q."""
@@ -259,6 +303,7 @@ def dense_verify_attn(kv, q, scale, out=None, out_dtype=torch.float32, workspace
     return out
 
 
+@_on_device
 def spec_sample(draft_logits, target_logits, draft_tokens, temperature, seed, offset,
                 out_tokens=None, num_accepted=None, workspace=None, stream=None):
     """Exact speculative sampling of one round; returns (out_tokens, num_accepted)."""

@@ -172,3 +172,19 @@ def test_misaligned_pointers_rejected():
     assert lib.s3r_kv_commit(kv, v, m, v, 4, v, None) == 1                             # v_new
     assert lib.s3r_kv_commit(kv, v, v, v, 4, m, None) == 1                             # bounds
     assert lib.s3r_spec_sample(2, 4, 100, v, v, v, 1.0, 0, 0, v, v, m, big, None) == 1  # workspace
+
+
+def test_binding_refuses_host_tensors():
+    """The Python binding only marshals device tensors; host tensors are refused
+    before the library is called."""
+    import torch
+
+    import self_sparse_speculative_paged_amd as s3r
+    d = torch.zeros((2, 4, 100))
+    t = torch.zeros((2, 5, 100))
+    x = torch.zeros((2, 4), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        s3r.spec_sample(d, t, x, 1.0, 0, 0)
+    with pytest.raises(ValueError):
+        s3r.PagedKVCache(torch.zeros((4, 2, 16, 64)), torch.zeros((4, 2, 64, 16)),
+                         torch.zeros((2, 2), dtype=torch.int32), torch.zeros(2, dtype=torch.int32), 4)
