@@ -194,7 +194,9 @@ def _sample_case(B, gamma, V, noise, seed, T=1.0):
 @pytest.mark.parametrize("B,gamma,V,noise,T", [
     (64, 4, 1024, 0.5, 1.0), (16, 6, 151936, 0.5, 1.0), (24, 8, 32000, 1.35, 1.0),
     (32, 2, 5000, 3.0, 1.0), (8, 3, 4099, 0.7, 0.6), (40, 1, 100, 0.0, 1.0),
-    (4, 16, 2001, 0.5, 1.0)])  # the longest draft the library takes
+    (4, 16, 2001, 0.5, 1.0),   # the longest draft the library takes
+    (8, 3, 1, 0.5, 1.0),       # one-token vocabulary: p = q = 1, every draft accepted
+    (16, 1, 2, 1.0, 1.0)])     # two tokens, one draft
 def test_spec_sample_matches_oracle(B, gamma, V, noise, T):
     d, t, x = _sample_case(B, gamma, V, noise, seed=B + V, T=T)
     out, n = s3r.spec_sample(d.to(DEV), t.to(DEV), x.to(DEV).int(), T, seed=0, offset=7)
@@ -202,8 +204,10 @@ def test_spec_sample_matches_oracle(B, gamma, V, noise, T):
     ro, rn, dec = oracle.spec_sample(d.double().numpy(), t.double().numpy(), x.numpy(), T, 0, 7)
     full = check_tokens(i32(out), i32(n), ro, rn, dec)
     assert full >= B // 2, (full, B)
-    if noise == 0.0:
+    if noise == 0.0 or V == 1:
         assert np.all(i32(n) == gamma)
+    if V == 1:
+        assert np.all(i32(out) == 0)
 
 
 @pytest.mark.parametrize("B,gamma,V,T", [(16, 4, 32000, 0.8), (8, 6, 151936, 1.0)])
