@@ -10,7 +10,9 @@ Each case runs every attention-side entry point and compares it with the oracle:
 - the once-per-round selection and the dense verify.
 
 The split sizes, wave counts and combine paths these shapes select are the ones the
-fixed cases do not enumerate. Tolerances are those of test_gpu_parity.py.
+fixed cases do not enumerate. Random KV commits (rollbacks, unallocated pages) and
+random sampling rounds (vocabularies of 1..20000, gamma up to 16, several
+temperatures) follow. Tolerances are those of test_gpu_parity.py.
 """
 import numpy as np
 import pytest
@@ -114,3 +116,67 @@ def test_random_shape_matches_oracle(seed):
     v_out = s3r.dense_verify_attn(kvc(gamma), wl.q_verify.to(DEV), scale)
     torch.cuda.synchronize()
     _attn_ok(v_out, oracle.dense_verify_attn(f64(wl.q_verify), K, V, P, Lv, scale), kv)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_kv_commit_matches_oracle(seed):
+    """Random commits: rows from a random first position, some past the
+    committed length (rolled back), an occasional unallocated page; pools and
+    bounds bit-exact against the oracle."""
+    rng = np.random.default_rng(2000 + seed)
+    Hkv = int(rng.choice([1, 2, 3, 8]))
+    D = int(rng.choice([64, 128]))
+    kv = "f32" if rng.random() < 0.3 else "bf16"
+    B = int(rng.integers(1, 6))
+    ctx = [int(x) for x in rng.integers(1, 800, size=B)]
+    count = int(rng.integers(0, 18))
+    slack = count + 2
+    print(f"random commit {seed}: Hkv={Hkv} D={D} kv={kv} ctx={ctx} count={count}", flush=True)
+    cfg = dict(B=B, Hq=Hkv, Hkv=Hkv, D=D, L=None, P=16, budget=64, gamma=slack, V=64, kv_dtype=kv,
+               draft_sd=2.0, noise_sd=0.7, temperature=1.0, heavy_pages=0)
+    wl = make_workload(cfg, device="cpu", seed=seed, ctx=ctx, with_logits=False)
+    pt = wl.page_table.clone()
+    if rng.random() < 0.5:  # one unallocated page past some sequence's start
+        b = int(rng.integers(0, B))
+        j = int(rng.integers(0, pt.shape[1]))
+        pt[b, j] = -1
+    first = np.array([max(0, L - 1 - int(rng.integers(0, 3))) for L in ctx], dtype=np.int32)
+    committed = np.array([max(0, int(f) + int(rng.integers(-3, count + 2))) for f in first], dtype=np.int32)
+    dt = wl.k_pool.dtype
+    g = torch.Generator().manual_seed(seed)
+    k_new = torch.randn((B, count, Hkv, D), generator=g).to(dt)
+    v_new = torch.randn((B, count, Hkv, D), generator=g).to(dt)
+    k_pool, v_pool, ptd = wl.k_pool.to(DEV), wl.v_pool.to(DEV), pt.to(DEV)
+    kvc0 = s3r.PagedKVCache(k_pool, v_pool, ptd, torch.from_numpy(np.array(ctx, dtype=np.int32)).to(DEV), Hkv)
+    bounds = torch.zeros((k_pool.shape[0], Hkv, 2, D), dtype=dt, device=DEV)
+    s3r.page_bounds_update(s3r.PagedKVCache(k_pool, v_pool, wl.page_table.to(DEV), kvc0.seq_lens, Hkv), bounds)
+    torch.cuda.synchronize()
+    K0, V0, B0 = f64(wl.k_pool), f64(wl.v_pool), f64(bounds)
+    rK, rV, rB = oracle.kv_commit(K0, V0, i32(pt), f64(k_new), f64(v_new), first, committed, B0)
+    kvc = s3r.PagedKVCache(k_pool, v_pool, ptd, torch.from_numpy(committed).to(DEV), Hkv)
+    s3r.kv_commit(kvc, k_new.to(DEV), v_new.to(DEV), torch.from_numpy(first).to(DEV), bounds)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(k_pool), rK) and np.array_equal(f64(v_pool), rV)
+    assert np.array_equal(f64(bounds), rB, equal_nan=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_spec_sample_matches_oracle(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.integers(1, 33))
+    gamma = int(rng.integers(1, 17))
+    V = int(rng.integers(1, 20000))
+    T = float(rng.choice([0.5, 0.8, 1.0, 1.3]))
+    noise = float(rng.choice([0.0, 0.3, 1.0, 2.5]))
+    print(f"random sample {seed}: B={B} gamma={gamma} V={V} T={T} noise={noise}", flush=True)
+    g = torch.Generator().manual_seed(seed)
+    d = torch.randn((B, gamma, V), generator=g) * 2.0
+    t = torch.cat([d + torch.randn((B, gamma, V), generator=g) * noise,
+                   torch.randn((B, 1, V), generator=g) * 2.0], dim=1)
+    x = oracle.draw_draft_tokens(d.double().numpy(), T, seed=seed, offset=0)
+    out, n = s3r.spec_sample(d.to(DEV), t.to(DEV), torch.from_numpy(x).to(DEV).int(), T, seed=seed, offset=5)
+    torch.cuda.synchronize()
+    ro, rn, dec = oracle.spec_sample(d.double().numpy(), t.double().numpy(), x, T, seed, 5)
+    from tests.parity import check_tokens
+    full = check_tokens(i32(out), i32(n), ro, rn, dec)
+    assert full >= B // 2, (full, B)
