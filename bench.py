@@ -390,6 +390,39 @@ def fidelity(args):
         return {"mean": round(float(v.mean()), 4), "p10": round(float(v.quantile(0.1)), 4),
                 "min": round(float(v.min()), 4)}
 
+    # Token level, through a toy head: logits = c_b * W o for a fixed random
+    # W [32768][Hq*D], with c_b set per sequence so the dense logits have sd 2
+    # (the workloads' draft-logit sd). p from the dense decode output at the
+    # step-0 query, q from the sparse draft output. Direct sparse sampling
+    # draws from q: its per-token distance from the dense policy is TV(p, q) =
+    # 1 - alpha. S3R draws from p exactly and accepts a draft with probability
+    # alpha = sum min(p, q), which spec_sample measures here.
+    V_TOY = 32768
+    W = torch.randn((V_TOY, Hq * D), generator=torch.Generator(device=dev).manual_seed(1), device=dev)
+    kv_d = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[0], Hq)
+    q0 = wl.draft_q(0)
+    o_dense = s3r.dense_verify_attn(kv_d, q0[:, None].contiguous(), scale)[:, 0].reshape(B, Hq * D)
+    z_dense = o_dense @ W.t()                                   # [B][V_TOY]
+    c = 2.0 / z_dense.std(dim=1, keepdim=True)
+    logp = torch.log_softmax(c * z_dense, dim=1)
+
+    def token_level(o_sparse, seed):
+        z = c * (o_sparse.reshape(B, Hq * D) @ W.t())
+        logq = torch.log_softmax(z, dim=1)
+        p, q = logp.exp(), logq.exp()
+        alpha = torch.minimum(p, q).sum(1)
+        tv = 1.0 - alpha
+        # S3R's own sampler on these logits: one draft drawn from q, verified against p
+        draft = z[:, None].contiguous()
+        target = torch.stack([c[:, 0, None] * z_dense, c[:, 0, None] * z_dense], dim=1).contiguous()
+        acc = []
+        for off in range(64):
+            x = torch.multinomial(q, 1, generator=torch.Generator(device=dev).manual_seed(seed * 100 + off)).int()
+            _, n = s3r.spec_sample(draft, target, x.contiguous(), 1.0, seed, off)
+            acc.append(n.float())
+        return {"tv_direct_sparse": stats(tv), "alpha": round(float(alpha.mean()), 4),
+                "s3r_measured_acceptance": round(float(torch.stack(acc).mean()), 4)}
+
     m0, mlast = page_mass(0), page_mass(gamma - 1)
     kv = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[0], Hq)
     bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=dev)
@@ -398,6 +431,7 @@ def fidelity(args):
         kv.set_seq_lens(wl.seq_lens[0])
         s3r.page_bounds_update(kv, bounds)
         sel0, _ = s3r.page_select(kv, bounds, wl.draft_q(0), budget, scale)
+        tok = token_level(s3r.sparse_draft_attn(kv, wl.draft_q(0), sel0, scale), seed=budget)
         _, sel_round, _ = s3r.sparse_draft_round(kv, bounds, wl.draft_q(0), budget, gamma, scale)
         kv.set_seq_lens(wl.seq_lens[gamma - 1])
         s3r.page_bounds_update(kv, bounds)
@@ -407,6 +441,7 @@ def fidelity(args):
             "fidelity": {"workload": f"{args.config}_layer", "budget_tokens": budget, "pages": k,
                          "draft_step": 0},
             "kept_mass": stats(kept(m0, sel0)), "best_k_pages": stats(best(m0, k)),
+            "token_level_toy_head": tok,
             "last_step": {"draft_step": gamma - 1,
                           "kept_mass_per_step_select": stats(kept(mlast, sel_last)),
                           "kept_mass_select_once": stats(kept(mlast, sel_round)),
