@@ -33,7 +33,11 @@ each query head's dense attention probability that falls on the selected pages
 (1 minus the total-variation distance between the sparse, renormalised and the
 dense attention distributions), at draft step 0 and at the round's last step for
 both selection frequencies, next to the best possible k pages. The dense
-probabilities are computed in fp32 with torch as the measuring stick.
+probabilities are computed in fp32 with torch as the measuring stick. At the
+token level, a fixed random head maps the dense and the sparse attention
+outputs to logits p and q: direct sparse sampling is TV(p, q) away from the
+dense policy per token, while S3R keeps p's law and accepts at alpha =
+sum min(p, q), which s3r_spec_sample measures on those logits.
 """
 import argparse
 import json
