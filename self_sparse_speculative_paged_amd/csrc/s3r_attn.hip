@@ -770,13 +770,10 @@ hipError_t launch_fused_draft(const AttnArgs& a, hipStream_t stream) {
     if (a.waves_per_group == 8) return launch_score_here<kD, 8, fused_topk_keys(8)>(a, grid, lds, stream);
     return hipErrorInvalidValue;
   }
-  switch (a.waves_per_group) {
-    case 1: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 1, kSelFromScores>), grid, dim3(64), lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 2, kSelFromScores>), grid, dim3(128), lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 4, kSelFromScores>), grid, dim3(256), lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelFromScores>), grid, dim3(512), lds, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  // Rank and attend after the score kernel: the draft-step plan always gives it
+  // eight waves, so its top-k runs on 512 threads.
+  if (a.waves_per_group != 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_bf16_kernel<kD, 1, true, 8, kSelFromScores>), grid, dim3(512), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_groups == 1) return e;
   hipLaunchKernelGGL((attn_combine_kernel<kD, true>), dim3((unsigned)((size_t)a.B * a.nq * a.Hq)),
