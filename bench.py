@@ -533,21 +533,13 @@ def _oracle_worker_init():
 def _oracle_slice(task):
     """One (sequence, kv head) slice of the round through the oracle, in a worker
     process. The slice's pages are gathered from the pools in shared memory
-    and upcast to fp64 (set-up, untimed, with the slice's page bounds). Then
-    gamma x (page_select + sparse draft), the dense verify and, for kv head 0,
-    the sequence's spec_sample run single-threaded. Returns (bytes, seconds)."""
+    and upcast to fp64 (set-up, untimed). Returns (bytes, seconds) of
+    `_run_oracle_slice`."""
     from multiprocessing import shared_memory
 
     import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle
 
     (names, shapes, bf16, idx, h, L, cfg, q_ver, logits) = task
-    P, D, Hq, Hkv, gamma, V = (cfg[k] for k in ("P", "D", "Hq", "Hkv", "gamma", "V"))
-    esz = 2 if bf16 else 4
-    scale = 1.0 / math.sqrt(D)
-    k = cfg["budget"] // P
     arrays = []
     for name, shape in zip(names, shapes):
         shm = shared_memory.SharedMemory(name=name)
@@ -560,9 +552,24 @@ def _oracle_slice(task):
             del pool, part
         finally:
             shm.close()
-    K, Vv = arrays
-    n = len(idx)
-    pt = np.arange(n, dtype=np.int64)[None, :]
+    return _run_oracle_slice(arrays[0], arrays[1], bf16, L, cfg, q_ver, logits)
+
+
+def _run_oracle_slice(K, Vv, bf16, L, cfg, q_ver, logits):
+    """The timed part of one slice: the slice's page bounds (untimed set-up),
+    then gamma x (page_select + sparse draft), the dense verify and, when
+    `logits` is given, the sequence's spec_sample, single-threaded. K and Vv
+    hold the slice's pages in order, fp64. Returns (bytes, seconds)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    P, D, gamma, V = (cfg[k] for k in ("P", "D", "gamma", "V"))
+    esz = 2 if bf16 else 4
+    scale = 1.0 / math.sqrt(D)
+    k = cfg["budget"] // P
+    pt = np.arange(K.shape[0], dtype=np.int64)[None, :]
     bounds = oracle.page_bounds(K, pt, np.array([L + gamma]))
     done = 0
     t0 = time.perf_counter()
@@ -582,6 +589,14 @@ def _oracle_slice(task):
     return done, time.perf_counter() - t0
 
 
+def _shm_free_bytes():
+    try:
+        st = os.statvfs("/dev/shm")
+        return st.f_bavail * st.f_frsize
+    except OSError:
+        return 0
+
+
 def cpu_baseline(wl, cfg, budget_s):
     """The oracle, as it stands, on the round's (sequence, kv head) slices, one
     slice per task over a pool of worker processes, one per host core of the
@@ -590,16 +605,51 @@ def cpu_baseline(wl, cfg, budget_s):
     value is the algorithmic bytes of the slices done over the wall time of
     the pool phase. The pools sit in host shared memory, copied once from the
     device before the clock starts. The wall time includes each worker's
-    gather and upcast of its slice."""
-    import multiprocessing as mp
-    from multiprocessing import shared_memory
+    gather and upcast of its slice.
 
+    Where /dev/shm cannot hold both pools (with a margin), the slices run in
+    this process instead, one core, each slice gathered from the device
+    before its clock starts; the value is then the bytes over the summed
+    slice times, and the sample says so."""
     import numpy as np
     import torch
 
     P, Hkv, Hq, gamma = (cfg[k] for k in ("P", "Hkv", "Hq", "gamma"))
     G = Hq // Hkv
     bf16 = cfg["kv_dtype"] == "bf16"
+
+    def slices():
+        for b in range(cfg["B"]):
+            L = int(wl.ctx[b])
+            idx = wl.page_table[b, :-(-(L + gamma) // P)].long()
+            logits = (wl.draft_logits[b:b + 1].to("cpu", torch.float64).numpy(),
+                      wl.target_logits[b:b + 1].to("cpu", torch.float64).numpy(),
+                      wl.draft_tokens[b:b + 1].cpu().numpy())
+            for h in range(Hkv):
+                q = wl.q_verify[b:b + 1, :, h * G:(h + 1) * G].to("cpu", torch.float64).numpy()
+                yield idx, h, L, q, logits if h == 0 else None
+
+    what = (f"each: {gamma} draft steps (page_select + sparse attention), dense verify of {gamma + 1} "
+            f"queries x {G} heads over the full context, plus spec_sample (vocab {cfg['V']}) "
+            f"once per sequence; fp64 NumPy")
+    need = sum(t.numel() * t.element_size() for t in (wl.k_pool, wl.v_pool))
+    if _shm_free_bytes() < need + need // 10 + (1 << 30):
+        total, spent, n = 0, 0.0, 0
+        t0 = time.perf_counter()
+        for idx, h, L, q, logits in slices():
+            if time.perf_counter() - t0 >= budget_s:
+                break
+            K, Vv = (t[idx, h:h + 1].to("cpu", torch.float64).numpy() for t in (wl.k_pool, wl.v_pool))
+            done, sec = _run_oracle_slice(K, Vv, bf16, L, cfg, q, logits)
+            total, spent, n = total + done, spent + sec, n + 1
+        return {"value": round(total / spent / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "bytes": total, "seconds": round(spent, 2),
+                "sample": f"{n} of the {cfg['B'] * Hkv} (sequence, kv head) slices of the round, {what}; "
+                          f"one process, 1 thread (/dev/shm too small for the pooled run)"}
+
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     shms, names, shapes = [], [], []
     try:
@@ -615,43 +665,28 @@ def cpu_baseline(wl, cfg, budget_s):
         ctx = mp.get_context("spawn")  # the workers never touch the GPU
         with ctx.Pool(workers, initializer=_oracle_worker_init) as pool:
             pool.map(abs, range(4 * workers))  # every worker started and initialised
-
-            def tasks():
-                for b in range(cfg["B"]):
-                    L = int(wl.ctx[b])
-                    idx = wl.page_table[b, :-(-(L + gamma) // P)].long().cpu().numpy()
-                    logits = (wl.draft_logits[b:b + 1].to("cpu", torch.float64).numpy(),
-                              wl.target_logits[b:b + 1].to("cpu", torch.float64).numpy(),
-                              wl.draft_tokens[b:b + 1].cpu().numpy())
-                    for h in range(Hkv):
-                        q = wl.q_verify[b:b + 1, :, h * G:(h + 1) * G].to("cpu", torch.float64).numpy()
-                        yield (names, shapes, bf16, idx, h, L, cfg, q, logits if h == 0 else None)
-
-            pending, total, slices = [], 0, 0
+            pending, total, n = [], 0, 0
             t0 = time.perf_counter()
-            for task in tasks():
+            for idx, h, L, q, logits in slices():
                 if time.perf_counter() - t0 >= budget_s:
                     break
+                task = (names, shapes, bf16, idx.cpu().numpy(), h, L, cfg, q, logits)
                 pending.append(pool.apply_async(_oracle_slice, (task,)))
                 while len(pending) >= 2 * workers:  # bounded host memory in flight
-                    done, _ = pending.pop(0).get()
-                    total += done
-                    slices += 1
+                    total += pending.pop(0).get()[0]
+                    n += 1
             for r in pending:
-                done, _ = r.get()
-                total += done
-                slices += 1
+                total += r.get()[0]
+                n += 1
             wall = time.perf_counter() - t0
     finally:
         for shm in shms:
             shm.close()
             shm.unlink()
     return {"value": round(total / wall / 1e9, 6), "unit": "GB/s", "cores": workers,
-            "kind": "oracle", "seconds": round(wall, 2),
-            "sample": f"{slices} of the {cfg['B'] * Hkv} (sequence, kv head) slices of the round, each: "
-                      f"{gamma} draft steps (page_select + sparse attention), dense verify of {gamma + 1} "
-                      f"queries x {G} heads over the full context, plus spec_sample (vocab {cfg['V']}) "
-                      f"once per sequence; fp64 NumPy, {workers} worker processes, 1 thread each"}
+            "kind": "oracle", "bytes": total, "seconds": round(wall, 2),
+            "sample": f"{n} of the {cfg['B'] * Hkv} (sequence, kv head) slices of the round, {what}, "
+                      f"{workers} worker processes, 1 thread each"}
 
 
 if __name__ == "__main__":
