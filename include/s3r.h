@@ -278,6 +278,9 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t 
  * U(b, slot, stream) = (w0 >> 11) * 2^-53 with w0 word 0 of Philox4x64-10
  * (Salmon et al., SC'11) at key (seed, 0), counter (offset, b, slot, stream).
  *   draft_logits  [B][gamma][V] fp32;  target_logits [B][gamma+1][V] fp32.
+ *                 -inf masks a token (probability 0). Every row needs at least
+ *                 one finite logit; NaN, +inf or a fully masked row give
+ *                 unspecified tokens (the writes stay inside out_tokens).
  *   draft_tokens  [B][gamma] int32 in [0, V).
  *   out_tokens    out [B][gamma+1] int32: accepted drafts, then the drawn token,
  *                 then -1.

@@ -216,9 +216,12 @@ __device__ void round_decision(const SampleArgs& a, int b, Round& rd) {
           rd.M[r] = M;
           rd.Z[r] = Z;
         } else {  // more than 64 chunks: fold this pass into the running values
+          // A side without mass adds nothing; rescaling it would form
+          // 0 * 2^(-inf - -inf) = NaN when every token so far is masked.
           const float Mn = fmaxf(rd.M[r], M);
-          rd.Z[r] = rd.Z[r] * exp2(((double)rd.M[r] - Mn) * c_log2) +
-                    Z * exp2(((double)M - Mn) * c_log2);
+          const double zr = rd.Z[r] > 0.0 ? rd.Z[r] * exp2(((double)rd.M[r] - Mn) * c_log2) : 0.0;
+          const double zp = Z > 0.0 ? Z * exp2(((double)M - Mn) * c_log2) : 0.0;
+          rd.Z[r] = zr + zp;
           rd.M[r] = Mn;
         }
         rd.iZ[r] = 1.0 / rd.Z[r];

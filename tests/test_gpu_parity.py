@@ -238,6 +238,27 @@ def test_spec_sample_masked_logits(B, gamma, V, T):
     assert np.any(gn < gamma)  # the masks make rejections happen
 
 
+def test_spec_sample_masked_leading_passes():
+    """A vocabulary of more than 128 chunks of 4096 tokens whose first 2 * 64
+    chunks are masked in every row: the row statistics fold two passes of 64
+    chunks without mass before the first pass with mass. The tokens follow
+    the oracle and lie in the unmasked tail."""
+    B, gamma, V, T = 4, 3, 600000, 1.0
+    masked = 2 * 64 * 4096
+    d, t, _ = _sample_case(B, gamma, V, 0.7, seed=77)
+    d[..., :masked] = float("-inf")
+    t[..., :masked] = float("-inf")
+    x = oracle.draw_draft_tokens(d.double().numpy(), T, seed=5, offset=0)
+    out, n = s3r.spec_sample(d.to(DEV), t.to(DEV), torch.from_numpy(x).to(DEV).int(), T, seed=2, offset=0)
+    torch.cuda.synchronize()
+    ro, rn, dec = oracle.spec_sample(d.double().numpy(), t.double().numpy(), x, T, 2, 0)
+    full = check_tokens(i32(out), i32(n), ro, rn, dec)
+    assert full >= B // 2, (full, B)
+    go, gn = i32(out), i32(n)
+    for b in range(B):
+        assert np.all(go[b, :gn[b] + 1] >= masked) and np.all(go[b, gn[b] + 1:] == -1), b
+
+
 def test_determinism_bitwise():
     wl = _make(_cfg("bf16", 128, 4, 2, 6), [900, 300], seed=21)
     kvc = _kv(wl, 6)
