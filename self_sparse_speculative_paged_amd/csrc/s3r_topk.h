@@ -29,6 +29,18 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Digit d of a radix histogram is counted at hist_slot(d). The digit scan has
+// lane l read the kPer digits kTopkBins - 1 - (kPer * l + e), e < kPer, so
+// lane l's digits are stored as one run of kPer slots. In a plain layout the
+// lanes of one read sit kPer dwords apart, so few LDS banks serve the whole
+// wave; rotating lane l's run by l / 4 spreads them over the banks.
+__device__ __forceinline__ int hist_slot(uint32_t digit) {
+  constexpr int kPer = kTopkBins / 64;
+  const int r = kTopkBins - 1 - (int)digit;
+  const int l = r / kPer;
+  return l * kPer + ((r % kPer + (l >> 2)) & (kPer - 1));
+}
+
 template <int kThreads>
 struct TopkShared {
   uint32_t hist[3][kTopkBins];
@@ -96,7 +108,7 @@ __device__ __forceinline__ void block_topk(const float* scores, int n, int k, To
     for (int e = 0; e < kR; ++e) {
       if (e >= nchunks) break;
       if (e * kThreads + tid < n && (key[e] & mask) == prefix)
-        atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+        atomicAdd(&hist[hist_slot((key[e] >> shift) & dmask)], 1u);
     }
     __syncthreads();
     // Lane l holds kPer consecutive bins counted from the top digit down; the
@@ -105,7 +117,7 @@ __device__ __forceinline__ void block_topk(const float* scores, int n, int k, To
     uint32_t cnt[kPer], own = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      cnt[e] = hist[kTopkBins - 1 - (kPer * lane + e)];
+      cnt[e] = hist[kPer * lane + ((e + (lane >> 2)) & (kPer - 1))];  // hist_slot of that digit
       own += cnt[e];
     }
     uint32_t above = wave_incl_scan(own) - own;
