@@ -66,12 +66,15 @@ class Round:
         s3r.spec_sample(self.wl.draft_logits, self.wl.target_logits, self.wl.draft_tokens, 1.0, 4, 1,
                         out_tokens=self.tok, num_accepted=self.nacc, workspace=self.ws_s)
 
+    def step(self, j):
+        self.kv.set_seq_lens(self.wl.seq_lens[j])
+        s3r.sparse_draft_step(self.kv, self.bounds, self.q[j], self.budget, self.scale,
+                              refresh_from=self.first[j], selected=self.sel, num_selected=self.nsel,
+                              out=self.d_out[j], workspace=self.ws_step)
+
     def per_step(self):
         for j in range(self.g):
-            self.kv.set_seq_lens(self.wl.seq_lens[j])
-            s3r.sparse_draft_step(self.kv, self.bounds, self.q[j], self.budget, self.scale,
-                                  refresh_from=self.first[j], selected=self.sel, num_selected=self.nsel,
-                                  out=self.d_out[j], workspace=self.ws_step)
+            self.step(j)
         self.verify_and_sample()
 
     def select_once(self):

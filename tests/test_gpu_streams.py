@@ -1,0 +1,94 @@
+"""Calls on separate streams at once give the results of one stream.
+
+The library keeps no state between calls, so calls on different streams
+whose outputs and workspaces are disjoint may overlap on the device. Two
+rounds of different workloads (a uniform and a ragged batch, each with its
+own bounds, outputs and workspaces) run concurrently:
+- on two streams from one host thread;
+- from two host threads, each with its own stream. The binding's ctypes calls
+  release the GIL, so both threads are inside the library at once.
+Every output equals the same round run alone, bit for bit.
+"""
+import threading
+
+import pytest
+import torch
+
+from tests.test_gpu_graph_replay import Round, _same, _workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _rounds():
+    rounds = [Round(_workload(False)), Round(_workload(True))]
+    refs = []
+    for r in rounds:
+        r.per_step()
+        torch.cuda.synchronize()
+        refs.append([t.clone() for t in r.outputs()])
+    return rounds, refs
+
+
+def _scramble(r):
+    for t in r.outputs()[:-1]:  # outputs (not the bounds) start from garbage
+        t.fill_(-3 if t.dtype == torch.int32 else 7.0)
+
+
+def _check(rounds, refs, tag):
+    for j, (r, ref) in enumerate(zip(rounds, refs)):
+        for i, (a, b) in enumerate(zip(r.outputs(), ref)):
+            assert _same(a, b), (tag, j, i)
+
+
+def test_two_streams_one_thread():
+    print("two rounds on two streams, one thread", flush=True)
+    rounds, refs = _rounds()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for r in rounds:
+            _scramble(r)
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        # interleave the two rounds' launches so that their kernels overlap
+        for j in range(rounds[0].g):
+            for r, s in zip(rounds, streams):
+                with torch.cuda.stream(s):
+                    r.step(j)
+        for r, s in zip(rounds, streams):
+            with torch.cuda.stream(s):
+                r.verify_and_sample()
+        torch.cuda.synchronize()
+        _check(rounds, refs, rep)
+
+
+def test_two_threads_two_streams():
+    print("two rounds from two host threads, a stream each", flush=True)
+    rounds, refs = _rounds()
+    errors = []
+    start = threading.Barrier(2)
+
+    def worker(r, dev):
+        try:
+            torch.cuda.set_device(dev)
+            s = torch.cuda.Stream()
+            start.wait()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    r.per_step()
+            s.synchronize()
+        except BaseException as e:  # reported by the main thread
+            errors.append(e)
+
+    for r in rounds:
+        _scramble(r)
+    torch.cuda.synchronize()
+    dev = torch.cuda.current_device()
+    threads = [threading.Thread(target=worker, args=(r, dev)) for r in rounds]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    _check(rounds, refs, "threads")
