@@ -293,6 +293,12 @@ def main():
     dv_gbs = (parts["draft"] + parts["verify"]) / (dv_us * 1e-6) / 1e9
 
     traffic = read_counter_traffic(args.config)
+    # The verify call is one kernel when its splits merge inside the workgroup
+    # (no workspace); otherwise a split combine and, on ragged batches, the
+    # longest-first ordering launch with it.
+    verify_label = ("dense_verify_attn: one attn_bf16_kernel launch, splits merged in the workgroup"
+                    if s3r.attn_workspace(kv, gamma + 1, wl.max_pages) == 0 else
+                    "dense_verify_attn: attn_bf16_kernel with its split combine / ordering launches")
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -327,7 +333,7 @@ def main():
             "accepted_tokens_per_s": round(mean_committed / (ms_once * 1e-3), 1),
             "step_bytes": int(sum(parts_once.values())),
         },
-        "roofline": {"kernel": "dense_verify_attn (attn_bf16_kernel + split combine)",
+        "roofline": {"kernel": verify_label,
                      "bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
