@@ -117,6 +117,8 @@ SELECT_CASES = [
     ("bf16", 128, 3, 2, 64, (700, 31)),
     ("bf16", 64, 7, 1, 48, (400, 200)),
     ("f32", 64, 5, 1, 32, (300, 64)),
+    ("bf16", 128, 4, 2, 100, (700, 90, 40)),    # budget not a multiple of P: k = 6
+    ("bf16", 64, 2, 2, 16, (500, 17, 1)),       # k = 1
 ]
 
 
@@ -361,6 +363,8 @@ FUSED_CASES = [
     ("bf16", 128, 4, 8, 512, tuple(60 + 97 * i for i in range(32))),
     ("bf16", 64, 8, 8, 256, tuple(3000 - 90 * i for i in range(32))),
     ("bf16", 128, 1, 8, 2048, tuple(2100 + 61 * i for i in range(32))),
+    ("bf16", 128, 4, 8, 1000, tuple(900 + 53 * i for i in range(32))),  # k = 62 over eight waves
+    ("bf16", 128, 4, 8, 16, tuple(300 + 7 * i for i in range(32))),    # k = 1: one wave attends
     ("f32", 64, 2, 2, 64, (512, 300)),         # fp32: the separate kernels
     # groups that are not a power of two take the score kernel + attention
     ("bf16", 128, 3, 2, 64, (700, 300)),
