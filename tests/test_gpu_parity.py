@@ -68,6 +68,9 @@ VERIFY_CASES = [
     ("bf16", 64, 5, 2, 2, (300, 33)),            # 15 rows: one row block
     ("bf16", 128, 7, 1, 8, (260, 40)),           # 63 rows: four row blocks
     ("f32", 128, 6, 1, 3, (200, 17)),            # 24 rows, fp32
+    # gamma = 0: one query per sequence, a plain dense decode step
+    ("bf16", 128, 4, 2, 0, (1000, 77, 1)),
+    ("f32", 64, 2, 2, 0, (300, 40)),
 ]
 
 
