@@ -112,6 +112,22 @@ def test_page_bounds_exact(kv, D):
     assert np.array_equal(f64(bounds)[used1], ref1[used1])
 
 
+@pytest.mark.parametrize("kv,D,span", [("bf16", 128, 4), ("f32", 64, 4), ("bf16", 64, 50)])
+def test_page_bounds_refresh_over_several_pages(kv, D, span):
+    """40 tokens appended past the bounds' length touch four pages (18 to 21
+    for L = 300): refreshed from first_pos with max_pages_touched = 4, or a
+    larger bound, they equal the oracle's bounds at the new length."""
+    wl = _make(_cfg(kv, D, gamma=40), [300, 17, 95], seed=13)
+    n_phys = wl.k_pool.shape[0]
+    bounds = torch.zeros((n_phys, 2, 2, D), dtype=wl.k_pool.dtype, device=DEV)
+    s3r.page_bounds_update(_kv(wl, 0), bounds)
+    s3r.page_bounds_update(_kv(wl, 40), bounds, first_pos=wl.seq_lens[0].clone(), max_pages_touched=span)
+    torch.cuda.synchronize()
+    ref = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), i32(wl.seq_lens[40]))
+    used = ~np.isnan(ref[:, 0, 0, 0])
+    assert np.array_equal(f64(bounds)[used], ref[used])
+
+
 SELECT_CASES = [
     ("bf16", 128, 4, 2, 64, (700, 300, 40)),
     ("bf16", 128, 2, 2, 160, (2000, 161)),
