@@ -70,6 +70,14 @@ def parse():
     return p.parse_args()
 
 
+def verify_algorithmic_flops(cfg, ctx):
+    """Flops of one dense verify by definition: query i of a sequence at
+    committed length L sees L + i positions, and each (q head, position) costs
+    2*D for q.k and 2*D for p*v."""
+    D, Hq, gamma = cfg["D"], cfg["Hq"], cfg["gamma"]
+    return sum(4 * D * Hq * sum(L + i for i in range(gamma + 1)) for L in ctx)
+
+
 def step_bytes(cfg, ctx, select_once=False):
     """Algorithmic HBM bytes of one round, summed over sequences. With
     select_once the bounds are read (and the tail page refreshed) at draft
@@ -287,12 +295,14 @@ def main():
     parts_once = step_bytes(cfg, ctx, select_once=True)
     gbs = total_bytes / (ms * 1e-3) / 1e9
     verify_gbs = parts["verify"] / (t_verify * 1e-6) / 1e9
+    verify_flops = verify_algorithmic_flops(cfg, ctx)
     per_step_draft = parts["draft"] / gamma
     draft_gbs = per_step_draft / (t_draft * 1e-6) / 1e9
     dv_us = gamma * t_draft + t_verify
     dv_gbs = (parts["draft"] + parts["verify"]) / (dv_us * 1e-6) / 1e9
 
     traffic = read_counter_traffic(args.config)
+    mfma = read_counter_mfma(args.config)
     # The verify call is one kernel when its splits merge inside the workgroup
     # (no workspace); otherwise a split combine and, on ragged batches, the
     # longest-first ordering launch with it.
@@ -337,6 +347,17 @@ def main():
                      "bound": "hbm", "achieved": round(verify_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(verify_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        # MFMA use of the same verify launch: algorithmic flops are 4 per
+        # (query row, visible token, d); the matrix cores also run the padding
+        # of the rows to 16-row blocks and P's second (lo) bf16 part.
+        "verify_mfma": {
+            "algorithmic_flops_per_launch": verify_flops,
+            "algorithmic_tflops": round(verify_flops / (t_verify * 1e-6) / 1e12, 1),
+            "mfma_flops_per_launch": mfma[1] if mfma else None,
+            "mfma_tflops": round(mfma[1] / (t_verify * 1e-6) / 1e12, 1) if mfma else None,
+            "peak_tflops_bf16": 2500.0,
+            "mfma_busy_pct": mfma[0] if mfma else None,
+        },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, cfg, args.cpu_seconds)
@@ -506,11 +527,12 @@ def sweep(args):
                     torch.cuda.empty_cache()
 
 
-def read_counter_traffic(config):
-    """HBM bytes per verify launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different kernel source."""
+def _profile_fields(name):
+    """The `key: value` fields of a committed rocprofv3 summary under profiles/,
+    or None when it is missing or was taken on a different attention kernel
+    source (its recorded hash no longer matches)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"counters_dense_verify_{config}.txt")
+    path = os.path.join(ROOT, "profiles", name)
     src = os.path.join(ROOT, "self_sparse_speculative_paged_amd", "csrc", "s3r_attn.hip")
     if not os.path.exists(path):
         return None
@@ -520,10 +542,24 @@ def read_counter_traffic(config):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if fields.get("kernel_source_sha256_16") != digest:
-        return None
+    return fields if fields.get("kernel_source_sha256_16") == digest else None
+
+
+def read_counter_traffic(config):
+    """HBM bytes per verify launch from the committed counter summary, or None."""
+    fields = _profile_fields(f"counters_dense_verify_{config}.txt")
     try:
-        return int(fields["hbm_bytes_per_launch"])
+        return int(fields["hbm_bytes_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def read_counter_mfma(config):
+    """(MFMA busy %, bf16 MFMA flops) per verify launch from the committed
+    counter summary, or None."""
+    fields = _profile_fields(f"counters_mfma_dense_verify_{config}.txt")
+    try:
+        return (float(fields["mfma_util_pct"]), int(fields["mfma_flops_bf16_per_launch"])) if fields else None
     except (KeyError, ValueError):
         return None
 

@@ -67,3 +67,24 @@ def test_ragged_bytes_follow_each_sequence():
             want[key] += v
     for key, v in want.items():
         assert got[key] == v, key
+
+
+def test_verify_flops_and_the_mfma_counter():
+    """The verify's algorithmic flops at the 8B shape (4 flops per query row,
+    visible position and d), and the bf16 MFMA flops rocprofv3 counted per
+    verify launch (profiles/) against what the kernel issues by design: rows
+    padded to 16-row blocks (28 -> 32), two MFMAs per P.V block (P split into a
+    hi and a lo bf16 part) and whole 32-token windows (2049 pages -> 1025)."""
+    import os
+
+    cfg = CONFIGS["qwen3_8b"]
+    B, L, gamma, D, Hq, Hkv = (cfg[k] for k in ("B", "L", "gamma", "D", "Hq", "Hkv"))
+    assert bench.verify_algorithmic_flops(cfg, [L] * B) == 4 * D * Hq * B * (7 * 32768 + 21) == 120270094336
+    path = os.path.join(os.path.dirname(bench.__file__), "profiles", "counters_mfma_dense_verify_qwen3_8b.txt")
+    fields = dict(line.split(":", 1) for line in open(path) if ":" in line)
+    counted = int(fields["mfma_flops_bf16_per_launch"])
+    rows = 32                                   # 28 rows in two 16-row blocks
+    windows = math.ceil(math.ceil((L + gamma) / cfg["P"]) / 2)
+    per_row_token = 2 * D + 2 * (2 * D)         # S = K.Q^T, then P_hi.V and P_lo.V
+    assert counted == per_row_token * rows * 32 * windows * B * Hkv
+    assert 0 < float(fields["mfma_util_pct"]) < 100
