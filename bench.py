@@ -28,6 +28,9 @@ one-layer autoregressive step), the committed tokens per round E, and the
 speedup E * t_dense / t_round next to the byte model's E * bytes_dense /
 bytes_round. One JSON line per point.
 
+--shrink runs the ragged long-tail batch as it drains: the round on its
+longest 128, 64, 16 and 8 sequences, one JSON line per active batch size.
+
 --fidelity measures what the sparse draft gives up: per budget, the share of
 each query head's dense attention probability that falls on the selected pages
 (1 minus the total-variation distance between the sparse, renormalised and the
@@ -65,6 +68,8 @@ def parse():
                    help="wall-time budget of the oracle baseline's worker-pool phase")
     p.add_argument("--sweep", action="store_true",
                    help="speedup-condition sweep instead of the one-round measurement")
+    p.add_argument("--shrink", action="store_true",
+                   help="the ragged batch as it drains: rounds on its longest 128, 64, 16 and 8 sequences")
     p.add_argument("--fidelity", action="store_true",
                    help="dense attention mass the page selection keeps, per budget")
     return p.parse_args()
@@ -238,6 +243,8 @@ def main():
         return sweep(args)
     if args.fidelity:
         return fidelity(args)
+    if args.shrink:
+        return shrink(args)
 
     import torch
 
@@ -525,6 +532,43 @@ def sweep(args):
                     }), flush=True)
                     del R, graphs
                     torch.cuda.empty_cache()
+
+
+def shrink(args):
+    """The ragged long-tail batch as it drains. Short rollouts finish first, so
+    the round runs on the longest 128, 64, 16 and 8 sequences of one lognormal
+    draw, kept in their original order, each on a fresh seeded workload. One
+    JSON line per active batch size."""
+    import torch
+
+    from s3r_inputs import CONFIGS, ragged_lengths
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS["ragged"]
+    full = ragged_lengths(cfg["B"], seed=0)
+    for n in cfg["shrink"]:
+        keep = torch.argsort(full, descending=True, stable=True)[:n].sort().values
+        ctx = [int(full[i]) for i in keep]
+        R = build_round("ragged", dev, seed=0, B=n, ctx=ctx)
+        graphs = []
+        ms = time_runner(make_runner(R.one_round, True, graphs), args.steps, args.warmup)
+        ms_once = time_runner(make_runner(R.one_round_select_once, True, graphs), args.steps, args.warmup)
+        parts = step_bytes(R.cfg, R.ctx)
+        once = sum(step_bytes(R.cfg, R.ctx, select_once=True).values())
+        gbs = sum(parts.values()) / (ms * 1e-3) / 1e9
+        _, committed = R.accept_stats()
+        print(json.dumps({
+            "shrink_point": {"active_batch": n, "context_min": min(ctx), "context_median": sorted(ctx)[n // 2],
+                             "context_max": max(ctx), "kv_gb": round(parts["verify"] / 1e9, 3)},
+            "round_ms": round(ms, 4), "value_gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "accepted_tokens_per_s": round(committed / (ms * 1e-3), 1),
+            "round_select_once_ms": round(ms_once, 4),
+            "select_once_gbs": round(once / (ms_once * 1e-3) / 1e9, 1),
+        }), flush=True)
+        del R, graphs
+        torch.cuda.empty_cache()
 
 
 def _profile_fields(name):
