@@ -38,7 +38,7 @@ def _run_fullsize(name, samples, shrink_to=None):
     wl = make_workload(name, device="cuda", seed=0)
     cfg = wl.cfg
     if shrink_to is not None:  # keep the longest sequences, as the long tail shrinks
-        keep = torch.argsort(wl.ctx, descending=True)[:shrink_to].sort().values
+        keep = torch.argsort(wl.ctx, descending=True, stable=True)[:shrink_to].sort().values
         wl.ctx = wl.ctx[keep]
         wl.page_table = wl.page_table[keep.to("cuda")].contiguous()
         wl.seq_lens = [s[keep.to("cuda")].contiguous() for s in wl.seq_lens]
@@ -174,6 +174,6 @@ def test_fullsize_aggressive():
     _run_fullsize("aggressive", [(3, 2), (15, 6)])
 
 
-@pytest.mark.parametrize("batch", [128, 8])
+@pytest.mark.parametrize("batch", [128, 64, 16, 8])  # the batch sizes bench.py --shrink times
 def test_fullsize_ragged(batch):
     _run_fullsize("ragged", [(0, 1), (5, 3), (batch - 1, 7)], shrink_to=batch)
