@@ -374,6 +374,7 @@ FUSED_CASES = [
     ("bf16", 128, 2, 2, 1024, (3000, 100)),    # selection longer than one workgroup's splits
     ("bf16", 64, 8, 1, 48, (333, 15)),
     ("bf16", 128, 4, 2, 4096, (100, 50)),      # budget covers every page
+    ("bf16", 128, 4, 2, 320000, (900, 30)),    # k = 20000: the list no longer fits LDS, three launches
     ("bf16", 64, 4, 2, 64, (8000, 7990)),      # 4 pages of 500, eight waves
     ("bf16", 128, 4, 2, 64, (9000, 200)),      # 4 pages of 563
     ("bf16", 64, 2, 1, 64, (140000, 300)),     # 8750 pages: past the fused top-k
