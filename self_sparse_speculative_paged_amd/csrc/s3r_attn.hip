@@ -246,11 +246,11 @@ __device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
 }
 
 // One row block (the draft, small verify groups) fits two waves per SIMD with a
-// 2-stage pipeline; more row blocks run one wave per SIMD with deeper stages.
-// Register pipeline depth per row-block count: what fits the registers of one
-// wave per SIMD (two waves for one row block) without spilling. Four row
-// blocks hold 64 rows of accumulators and queries; a second stage spills there
-// and runs 2.5x slower than a single one.
+// 2-stage pipeline. Two row blocks run one wave per SIMD with three stages;
+// three and four row blocks keep two and one, since their accumulators and
+// queries take the registers. Each depth is what fits one wave per SIMD (two
+// for one row block) without spilling: at four row blocks a second stage
+// spills and runs 2.5x slower than a single one.
 template <int kNB>
 constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : (kNB == 3 ? 2 : 1)); }
 template <int kNB>
