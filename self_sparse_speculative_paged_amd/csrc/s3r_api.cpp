@@ -222,6 +222,24 @@ struct SingleKernelPlan {
   int32_t pt_offset, list_offset;
 };
 
+// A four-wave workgroup runs at about half its CU's rate while it shares the
+// CU. Four waves are only worth it while the longest (sequence, kv head) then
+// still ends near the average CU's load. Otherwise, on a ragged batch whose
+// long outliers meet few (sequence, kv head) pairs per CU, their workgroups
+// would set the end of the kernel. The bytes of one item with p pages are its
+// bounds (p rows) plus the K/V of min(k, p) pages. The batch total comes from
+// the page hint.
+bool longest_fits_half_cu(const s3r_paged_kv& kv, int32_t k, int32_t cus) {
+  const double bound_bytes = 2.0 * kv.head_dim * 2, page_bytes = 2.0 * kv.page_size * kv.head_dim * 2;
+  auto item = [&](double pages) { return pages * bound_bytes + (pages < k ? pages : k) * page_bytes; };
+  const double total = kv.total_pages_hint > 0 ? kv.total_pages_hint
+                                               : (double)kv.num_seqs * kv.max_pages_per_seq;
+  const double per_cu = kv.num_kv_heads * (total * bound_bytes +
+                                           kv.num_seqs * (total / kv.num_seqs < k ? total / kv.num_seqs : k) *
+                                               page_bytes) / cus;
+  return 2.0 * item(kv.max_pages_per_seq) <= 1.25 * per_cu;
+}
+
 SingleKernelPlan plan_single_kernel(const s3r_paged_kv& kv, int32_t k) {
   SingleKernelPlan p{};
   const int32_t G = kv.num_q_heads / kv.num_kv_heads;
@@ -234,7 +252,10 @@ SingleKernelPlan plan_single_kernel(const s3r_paged_kv& kv, int32_t k) {
   // two share each CU at once, so one's ranking overlaps the other's reads.
   // Their 256-thread top-k ranks up to kWideTopkKeys * 256 pages.
   const int kWaves =
-      items >= 2 * (int64_t)cus && kv.max_pages_per_seq <= s3r::kWideTopkKeys * 64 * 4 ? 4 : 8;
+      items >= 2 * (int64_t)cus && kv.max_pages_per_seq <= s3r::kWideTopkKeys * 64 * 4 &&
+              longest_fits_half_cu(kv, k, cus)
+          ? 4
+          : 8;
   const int keys = kWaves == 4 ? s3r::kWideTopkKeys : s3r::fused_topk_keys(kWaves);
   if (kv.max_pages_per_seq > keys * 64 * kWaves) return p;
   const s3r::SplitPlan& a = p.attn = wave_plan(kv, k, kWaves);
