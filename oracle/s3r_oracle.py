@@ -31,7 +31,9 @@ written out:
 Pins (tests/test_oracle_*.py): brute-force bounds and sort, torch SDPA on CPU,
 a second streaming-softmax decode path, exact rational enumeration of the
 sampler at vocab 8, chi-square Monte Carlo, q = p => full acceptance, the
-accepted-length law prod(alpha_i), and numpy.random.Philox known answers.
+accepted-length law prod(alpha_i), numpy.random.Philox known answers, and for
+the acceptance rate its closed forms (q = p, disjoint supports, two tokens),
+the total-variation identity and the enumerated accept probability.
 Parity of the page-level figures (attention share, end-to-end speedup) is
 unpinned: they need the model and workloads the pages measured.
 
@@ -57,7 +59,7 @@ __all__ = [
     "page_bounds", "page_scores", "page_select", "round_forced_pages", "page_select_round",
     "kv_commit",
     "attend", "sparse_draft_attn", "dense_verify_attn", "decode_streaming",
-    "softmax", "icdf", "spec_sample", "draw_draft_tokens",
+    "softmax", "icdf", "spec_sample", "draw_draft_tokens", "draw_tokens", "acceptance_rate",
 ]
 
 # ---------------------------------------------------------------------------
@@ -485,12 +487,51 @@ def spec_sample(draft_logits, target_logits, draft_tokens, temperature, seed, of
     return out, n_acc, decisions
 
 
+def draw_tokens(logits, temperature, seed, offset, first_slot=0):
+    """Direct sampling from a row's own softmax: the drafter's draws.
+
+    S3R Abstract: the sparse-attention policy proposes tokens; sampling from it
+    directly, with no dense check, is the comparator the abstract calls
+    unstable. Row r of sequence b (logits[b][r], one draft position) draws
+      x[b][r] = ICDF(softmax(logits[b][r] / T), U(b, first_slot + r, 2)),
+    stream 2 being the drafter's own uniforms; first_slot lets a drafter that
+    samples one position at a time use the slot of that position.
+
+    Returns (x[B][R] int32, margin[B][R]) with margin as in icdf().
+    """
+    B, R, _ = logits.shape
+    x = np.empty((B, R), dtype=np.int32)
+    margin = np.empty((B, R))
+    for b in range(B):
+        for r in range(R):
+            x[b, r], margin[b, r] = icdf(softmax(logits[b, r], temperature),
+                                         uniform(seed, offset, b, first_slot + r, 2))
+    return x, margin
+
+
 def draw_draft_tokens(draft_logits, temperature, seed, offset):
     """x[b][i] = ICDF(q_i, U(b, i, 2)): the drafter's own draws from q_i."""
+    return draw_tokens(draft_logits, temperature, seed, offset)[0]
+
+
+def acceptance_rate(draft_logits, target_logits, temperature):
+    """alpha[b][i] = sum_x min(p_i(x), q_i(x)) for the gamma draft positions.
+
+    p_i = softmax(target_logits[b][i] / T), q_i = softmax(draft_logits[b][i] / T).
+    Under the speculative-sampling rule (the titles the S3R reference list
+    cites) a draft x ~ q_i is accepted with probability min(1, p_i(x)/q_i(x)),
+    so the chance of accepting position i is sum_x q_i(x) min(1, p_i/q_i) =
+    alpha_i; and 1 - alpha_i is the total-variation distance TV(p_i, q_i), how
+    far one token sampled directly from the sparse policy is from the dense
+    policy's law (the direct-sparse-sampling comparator of the S3R Abstract).
+    target_logits may hold gamma + 1 rows; the bonus row has no draft partner
+    and is not used. Returns alpha[B][gamma] float64.
+    """
     B, gamma, _ = draft_logits.shape
-    x = np.empty((B, gamma), dtype=np.int32)
+    alpha = np.empty((B, gamma))
     for b in range(B):
         for i in range(gamma):
-            x[b, i] = icdf(softmax(draft_logits[b, i], temperature),
-                           uniform(seed, offset, b, i, 2))[0]
-    return x
+            p = softmax(target_logits[b, i], temperature)
+            q = softmax(draft_logits[b, i], temperature)
+            alpha[b, i] = float(np.minimum(p, q).sum())
+    return alpha

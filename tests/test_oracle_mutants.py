@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 import oracle.s3r_oracle as om
+from tests import test_oracle_acceptance as tacc
 from tests import test_oracle_attention as ta
 from tests import test_oracle_kv_commit as tk
 from tests import test_oracle_philox as tp
@@ -65,6 +66,12 @@ SAMPLE = [ts.test_icdf_edges, ts.test_output_format] + [
     lambda a=a: ts.test_exact_enumeration_vocab8(*a) for a in [(0, 2, 1.0), (2, 2, 0.7), (1, 3, 1.0)]] + [
     ts.test_q_equals_p_accepts_everything, ts.test_monte_carlo_chi_square_vocab1024,
     ts.test_accepted_length_law]
+DIRECT = [tacc.test_acceptance_q_equals_p_is_one, tacc.test_acceptance_disjoint_supports_is_zero] + [
+    lambda a=a: tacc.test_acceptance_two_tokens_closed_form(*a) for a in [(1.5, -0.5, 1.0), (3.0, 2.0, 0.5)]] + [
+    lambda a=a: tacc.test_acceptance_is_one_minus_total_variation(*a) for a in [(2, 1.0), (3, 0.7)]] + [
+    lambda a=a: tacc.test_acceptance_equals_enumerated_accept_probability(*a) for a in [(5, 1.0), (6, 0.7)]] + [
+    lambda s=s: tacc.test_draws_follow_the_definition_on_stream_2(s) for s in (0, 3)] + [
+    tacc.test_one_position_at_a_time_equals_all_at_once]
 
 # (case, function, expression in the oracle, planted replacement, pins)
 MUTANTS = [
@@ -143,6 +150,19 @@ MUTANTS = [
      SAMPLE),
     ("softmax_ignores_temperature", "softmax", "np.float64) / temperature", "np.float64)", SAMPLE),
     ("icdf_non_strict", "icdf", "c > target", "c >= target", SAMPLE),
+    # direct sparse sampling: the drafter's draws and the acceptance rate
+    ("alpha_max_not_min", "acceptance_rate", "np.minimum(p, q)", "np.maximum(p, q)", DIRECT),
+    ("alpha_next_target_row", "acceptance_rate", "target_logits[b, i], temperature",
+     "target_logits[b, i + 1], temperature", DIRECT),
+    ("alpha_without_temperature", "acceptance_rate", "softmax(draft_logits[b, i], temperature)",
+     "softmax(draft_logits[b, i], 1.0)", DIRECT),
+    ("alpha_unnormalised_min", "acceptance_rate", "np.minimum(p, q).sum()", "np.minimum(p, q).max()", DIRECT),
+    ("draws_on_the_residual_stream", "draw_tokens", "uniform(seed, offset, b, first_slot + r, 2)",
+     "uniform(seed, offset, b, first_slot + r, 1)", DIRECT),
+    ("draws_ignore_first_slot", "draw_tokens", "uniform(seed, offset, b, first_slot + r, 2)",
+     "uniform(seed, offset, b, r, 2)", DIRECT),
+    ("draws_without_temperature", "draw_tokens", "softmax(logits[b, r], temperature)",
+     "softmax(logits[b, r], 1.0)", DIRECT),
 ]
 
 
@@ -160,6 +180,6 @@ def test_pins_catch_planted_mistake(case, fn, old, new, pins, monkeypatch):
 
 
 def test_unplanted_oracle_passes_every_pin():
-    for pins in (PHILOX, SELECT, ROUND, ATTENTION, COMMIT, SAMPLE):
+    for pins in (PHILOX, SELECT, ROUND, ATTENTION, COMMIT, SAMPLE, DIRECT):
         for pin in pins:
             pin()

@@ -178,6 +178,8 @@ def test_accepted_length_law():
     x = oracle.draw_draft_tokens(draft, 1.0, seed=9, offset=1)
     _, n, _ = oracle.spec_sample(draft, target, x, 1.0, seed=9, offset=1)
     alpha = [np.minimum(_softmax(target[0, i]), _softmax(draft[0, i])).sum() for i in range(gamma)]
+    # the oracle's acceptance rate is the same law's per-position factor
+    np.testing.assert_allclose(oracle.acceptance_rate(draft[:1], target[:1], 1.0)[0], alpha, rtol=0, atol=1e-12)
     for k in range(1, gamma + 1):
         expect = np.prod(alpha[:k])
         got = np.mean(n >= k)
