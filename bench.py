@@ -147,6 +147,21 @@ def build_round(config, dev, seed=0, **overrides):
     ws_s = torch.empty(max(1, s3r.spec_sample_workspace(B, gamma, V)), dtype=torch.uint8, device=dev)
     out_tok = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
     n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    # The drafter's own tokens: each sequence's gamma draft rows sampled by the
+    # library (the Philox stream the drafter owns), as a drafter would.
+    draft_tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    ws_draw = torch.empty(max(1, s3r.draft_sample_workspace(B, gamma, V)), dtype=torch.uint8, device=dev)
+    ws_alpha = torch.empty(max(1, s3r.acceptance_rate_workspace(B, gamma, V)), dtype=torch.uint8,
+                           device=dev)
+    alpha = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+
+    def draft_draws(offset=0):
+        s3r.draft_sample(wl.draft_logits, T, 0, offset, tokens=draft_tokens, workspace=ws_draw)
+
+    def acceptance():
+        s3r.acceptance_rate(wl.draft_logits, wl.target_logits, T, alpha=alpha, workspace=ws_alpha)
+
+    draft_draws(0)
 
     def draft_step(j):
         kv.set_seq_lens(wl.seq_lens[j])
@@ -158,7 +173,7 @@ def build_round(config, dev, seed=0, **overrides):
         s3r.dense_verify_attn(kv, wl.q_verify, scale, out=v_out, workspace=ws_v)
 
     def sample(offset):
-        s3r.spec_sample(wl.draft_logits, wl.target_logits, wl.draft_tokens, T, 0, offset,
+        s3r.spec_sample(wl.draft_logits, wl.target_logits, draft_tokens, T, 0, offset,
                         out_tokens=out_tok, num_accepted=n_acc, workspace=ws_s)
 
     def one_round(offset=0):
@@ -290,6 +305,10 @@ def main():
     t_verify = time_call(lambda: s3r.dense_verify_attn(kv, wl.q_verify, scale, out=R.v_out,
                                                        workspace=R.ws_v), reps)
     t_sample = time_call(lambda: R.sample(0), reps)
+    t_draw = time_call(lambda: R.draft_draws(0), reps)
+    t_alpha = time_call(R.acceptance, reps)
+    R.acceptance()
+    mean_alpha = float(R.alpha.mean())
     # KV commit of a verify's gamma+1 rows at the round's positions (last: it rewrites them).
     g = torch.Generator(device=dev).manual_seed(1)
     k_new = torch.randn((B, gamma + 1, Hkv, D), device=dev, generator=g).to(wl.k_pool.dtype)
@@ -343,7 +362,9 @@ def main():
         "launch_us": {"page_bounds_update": round(t_bounds, 2), "page_select": round(t_select, 2),
                       "sparse_draft_attn": round(t_draft, 2), "sparse_draft_step": round(t_step, 2),
                       "dense_verify_attn": round(t_verify, 2), "spec_sample": round(t_sample, 2),
-                      "kv_commit": round(t_commit, 2)},
+                      "kv_commit": round(t_commit, 2), "draft_sample": round(t_draw, 2),
+                      "acceptance_rate": round(t_alpha, 2)},
+        "mean_alpha": round(mean_alpha, 4),
         "select_once": {
             "ms_per_step": round(ms_once, 4),
             "value": round(sum(parts_once.values()) / (ms_once * 1e-3) / 1e9, 1),

@@ -295,6 +295,54 @@ s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
                            uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * s3r_draft_sample: the drafter's own draws, sampling directly from the
+ * sparse policy (S3R Abstract: sparse attention proposes the tokens; sampling
+ * from that policy with no dense check is the direct-sparse-sampling
+ * comparator the abstract finds unstable). Row r of sequence b draws
+ *   tokens[b][r] = ICDF(softmax(logits[b][r] / T), U(b, first_slot + r, 2)),
+ * ICDF and U as in s3r_spec_sample; stream 2 is the drafter's, so these draws
+ * are independent of the sampler's accept (0) and residual (1) uniforms. With
+ * first_slot = 0 and n_rows = gamma the tokens are the draft_tokens input of
+ * s3r_spec_sample; a drafter that samples one position at a time passes
+ * n_rows = 1 and first_slot = that position's draft index.
+ *   logits      [B][n_rows][V] fp32; -inf masks a token. Every row needs a
+ *               finite logit (a fully masked row gives an unspecified token
+ *               in [-1, V)).
+ *   first_slot  >= 0.
+ *   tokens      out [B][n_rows] int32 in [0, V).
+ * Errors: INVALID_ARGUMENT for NULL pointers, num_seqs, n_rows or vocab < 1,
+ * first_slot < 0, temperature not finite and > 0; UNSUPPORTED when
+ * num_seqs * n_rows * ceil(vocab / 4096) >= 2^31; WORKSPACE_TOO_SMALL.
+ * Deterministic; two launches (chunk statistics, then one draw per row).
+ */
+size_t s3r_draft_sample_workspace(int32_t num_seqs, int32_t n_rows, int32_t vocab);
+s3r_status s3r_draft_sample(int32_t num_seqs, int32_t n_rows, int32_t vocab, const float* logits,
+                            float temperature, uint64_t seed, uint64_t offset, int64_t first_slot,
+                            int32_t* tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_acceptance_rate: per draft position, the probability that exact
+ * speculative sampling accepts a draft drawn from q_i,
+ *   alpha[b][i] = sum_x min(p_i(x), q_i(x)),  i = 0..gamma-1,
+ * with p_i = softmax(target_logits[b][i] / T), q_i = softmax(draft_logits[b][i] / T).
+ * 1 - alpha is the total-variation distance TV(p_i, q_i): how far a token
+ * sampled directly from the sparse policy is from the dense policy's law,
+ * the gap that S3R turns into a lower acceptance rate instead (S3R Abstract).
+ *   draft_logits [B][gamma][V], target_logits [B][gamma+1][V] fp32 (the
+ *                layouts of s3r_spec_sample; the bonus row is not read).
+ *   alpha        out [B][gamma] double, 8-byte aligned.
+ * Errors: INVALID_ARGUMENT for NULL or misaligned pointers, num_seqs, gamma
+ * or vocab < 1, temperature not finite and > 0; UNSUPPORTED when
+ * num_seqs * 2 * gamma * ceil(vocab / 4096) >= 2^31; WORKSPACE_TOO_SMALL.
+ * Deterministic: fp64 sums in a fixed order.
+ */
+size_t s3r_acceptance_rate_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab);
+s3r_status s3r_acceptance_rate(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                               const float* draft_logits, const float* target_logits,
+                               float temperature, double* alpha, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (host, never NULL). */
 const char* s3r_status_string(s3r_status status);
 /* Library version: major * 10000 + minor * 100 + patch. */

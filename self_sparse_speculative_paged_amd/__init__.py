@@ -10,7 +10,9 @@ Entry points (same names as include/s3r.h without the prefix):
   page_bounds_update, page_select, sparse_draft_attn, sparse_draft_step (the
   three fused), sparse_draft_round (a draft step whose selection the round's
   later steps reuse), kv_commit (write new K/V rows, keep the bounds exact,
-  roll back), dense_verify_attn, spec_sample, and the workspace queries.
+  roll back), dense_verify_attn, spec_sample, draft_sample (the drafter's own
+  draws from its logits), acceptance_rate (alpha = sum min(p, q) per draft
+  position), and the workspace queries.
 """
 import ctypes
 import functools
@@ -25,7 +27,8 @@ __all__ = [
     "S3RError", "PagedKVCache", "page_bounds_update", "page_select", "sparse_draft_attn",
     "dense_verify_attn", "spec_sample", "page_select_workspace", "attn_workspace",
     "spec_sample_workspace", "version", "sparse_draft_step", "sparse_draft_step_workspace",
-    "sparse_draft_round", "kv_commit",
+    "sparse_draft_round", "kv_commit", "draft_sample", "draft_sample_workspace",
+    "acceptance_rate", "acceptance_rate_workspace",
 ]
 
 _KV_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
@@ -149,9 +152,20 @@ def spec_sample_workspace(num_seqs, gamma, vocab):
     return _lib.load().s3r_spec_sample_workspace(num_seqs, gamma, vocab)
 
 
-def _workspace(nbytes, like, workspace):
+def _alloc(shape, dtype, device, stream):
+    """A tensor the call allocates for itself. torch's caching allocator ties
+    a block to the stream it was allocated on; when the call runs on another
+    stream, the block is also recorded on that one, so it is not handed out
+    again while the call's kernels may still use it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
+def _workspace(nbytes, like, workspace, stream=None):
     if workspace is None:
-        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+        workspace = _alloc((max(int(nbytes), 1),), torch.uint8, like.device, stream)
     _dev(workspace, "workspace", torch.uint8)
     return workspace
 
@@ -175,10 +189,10 @@ def page_select(kv, bounds, q, budget_tokens, scale, selected=None, num_selected
     lib = _lib.load()
     k = budget_tokens // kv.P
     if selected is None:
-        selected = torch.empty((kv.B, kv.Hkv, k), dtype=torch.int32, device=q.device)
+        selected = _alloc((kv.B, kv.Hkv, k), torch.int32, q.device, stream)
     if num_selected is None:
-        num_selected = torch.empty((kv.B,), dtype=torch.int32, device=q.device)
-    ws = _workspace(page_select_workspace(kv, budget_tokens), q, workspace)
+        num_selected = _alloc((kv.B,), torch.int32, q.device, stream)
+    ws = _workspace(page_select_workspace(kv, budget_tokens), q, workspace, stream)
     n_phys = kv.k_pool.shape[0]
     _check(lib.s3r_page_select(
         kv.ref(), _dev(bounds, "bounds", kv.dtype, (n_phys, kv.Hkv, 2, kv.D)),
@@ -199,8 +213,8 @@ def sparse_draft_attn(kv, q, selected, scale, out=None, out_dtype=torch.float32,
     lib = _lib.load()
     k = selected.shape[-1]
     if out is None:
-        out = torch.empty((kv.B, kv.num_q_heads, kv.D), dtype=out_dtype, device=q.device)
-    ws = _workspace(attn_workspace(kv, 1, k), q, workspace)
+        out = _alloc((kv.B, kv.num_q_heads, kv.D), out_dtype, q.device, stream)
+    ws = _workspace(attn_workspace(kv, 1, k), q, workspace, stream)
     _check(lib.s3r_sparse_draft_attn(
         kv.ref(), _dev(q, "q", kv.dtype, (kv.B, kv.num_q_heads, kv.D)),
         _dev(selected, "selected", torch.int32, (kv.B, kv.Hkv, k)), k, float(scale),
@@ -222,12 +236,12 @@ def sparse_draft_step(kv, bounds, q, budget_tokens, scale, refresh_from=None, se
     lib = _lib.load()
     k = budget_tokens // kv.P
     if selected is None:
-        selected = torch.empty((kv.B, kv.Hkv, k), dtype=torch.int32, device=q.device)
+        selected = _alloc((kv.B, kv.Hkv, k), torch.int32, q.device, stream)
     if num_selected is None:
-        num_selected = torch.empty((kv.B,), dtype=torch.int32, device=q.device)
+        num_selected = _alloc((kv.B,), torch.int32, q.device, stream)
     if out is None:
-        out = torch.empty((kv.B, kv.num_q_heads, kv.D), dtype=out_dtype, device=q.device)
-    ws = _workspace(sparse_draft_step_workspace(kv, budget_tokens), q, workspace)
+        out = _alloc((kv.B, kv.num_q_heads, kv.D), out_dtype, q.device, stream)
+    ws = _workspace(sparse_draft_step_workspace(kv, budget_tokens), q, workspace, stream)
     n_phys = kv.k_pool.shape[0]
     rf = None if refresh_from is None else _dev(refresh_from, "refresh_from", torch.int32, (kv.B,))
     _check(lib.s3r_sparse_draft_step(
@@ -251,12 +265,12 @@ def sparse_draft_round(kv, bounds, q, budget_tokens, gamma, scale, refresh_from=
     lib = _lib.load()
     k = budget_tokens // kv.P
     if selected is None:
-        selected = torch.empty((kv.B, kv.Hkv, k), dtype=torch.int32, device=q.device)
+        selected = _alloc((kv.B, kv.Hkv, k), torch.int32, q.device, stream)
     if num_selected is None:
-        num_selected = torch.empty((kv.B,), dtype=torch.int32, device=q.device)
+        num_selected = _alloc((kv.B,), torch.int32, q.device, stream)
     if out is None:
-        out = torch.empty((kv.B, kv.num_q_heads, kv.D), dtype=out_dtype, device=q.device)
-    ws = _workspace(sparse_draft_step_workspace(kv, budget_tokens), q, workspace)
+        out = _alloc((kv.B, kv.num_q_heads, kv.D), out_dtype, q.device, stream)
+    ws = _workspace(sparse_draft_step_workspace(kv, budget_tokens), q, workspace, stream)
     n_phys = kv.k_pool.shape[0]
     rf = None if refresh_from is None else _dev(refresh_from, "refresh_from", torch.int32, (kv.B,))
     _check(lib.s3r_sparse_draft_round(
@@ -294,8 +308,8 @@ def dense_verify_attn(kv, q, scale, out=None, out_dtype=torch.float32, workspace
     nq = q.shape[1]
     shape = (kv.B, nq, kv.num_q_heads, kv.D)
     if out is None:
-        out = torch.empty(shape, dtype=out_dtype, device=q.device)
-    ws = _workspace(attn_workspace(kv, nq, kv.max_pages), q, workspace)
+        out = _alloc(shape, out_dtype, q.device, stream)
+    ws = _workspace(attn_workspace(kv, nq, kv.max_pages), q, workspace, stream)
     _check(lib.s3r_dense_verify_attn(
         kv.ref(), _dev(q, "q", kv.dtype, shape), nq, float(scale), _OUT_DTYPES[out.dtype],
         _dev(out, "out", None, shape), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
@@ -310,10 +324,10 @@ def spec_sample(draft_logits, target_logits, draft_tokens, temperature, seed, of
     lib = _lib.load()
     B, gamma, V = draft_logits.shape
     if out_tokens is None:
-        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=draft_logits.device)
+        out_tokens = _alloc((B, gamma + 1), torch.int32, draft_logits.device, stream)
     if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=draft_logits.device)
-    ws = _workspace(spec_sample_workspace(B, gamma, V), draft_logits, workspace)
+        num_accepted = _alloc((B,), torch.int32, draft_logits.device, stream)
+    ws = _workspace(spec_sample_workspace(B, gamma, V), draft_logits, workspace, stream)
     _check(lib.s3r_spec_sample(
         B, gamma, V, _dev(draft_logits, "draft_logits", torch.float32),
         _dev(target_logits, "target_logits", torch.float32, (B, gamma + 1, V)),
@@ -322,3 +336,46 @@ def spec_sample(draft_logits, target_logits, draft_tokens, temperature, seed, of
         _dev(num_accepted, "num_accepted", torch.int32, (B,)),
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)), "s3r_spec_sample")
     return out_tokens, num_accepted
+
+
+def draft_sample_workspace(num_seqs, n_rows, vocab):
+    return _lib.load().s3r_draft_sample_workspace(num_seqs, n_rows, vocab)
+
+
+def acceptance_rate_workspace(num_seqs, gamma, vocab):
+    return _lib.load().s3r_acceptance_rate_workspace(num_seqs, gamma, vocab)
+
+
+@_on_device
+def draft_sample(logits, temperature, seed, offset, first_slot=0, tokens=None, workspace=None,
+                 stream=None):
+    """The drafter's own draws from logits [B][n_rows][V]: row r of sequence b
+    samples softmax(logits[b][r] / T) with the Philox uniform U(b, first_slot + r, 2);
+    returns tokens [B][n_rows] int32."""
+    lib = _lib.load()
+    B, R, V = logits.shape
+    if tokens is None:
+        tokens = _alloc((B, R), torch.int32, logits.device, stream)
+    ws = _workspace(draft_sample_workspace(B, R, V), logits, workspace, stream)
+    _check(lib.s3r_draft_sample(
+        B, R, V, _dev(logits, "logits", torch.float32), float(temperature), int(seed), int(offset),
+        int(first_slot), _dev(tokens, "tokens", torch.int32, (B, R)), ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), _stream(stream)), "s3r_draft_sample")
+    return tokens
+
+
+@_on_device
+def acceptance_rate(draft_logits, target_logits, temperature, alpha=None, workspace=None, stream=None):
+    """alpha [B][gamma] float64 = sum_x min(p_i, q_i) per draft position
+    (1 - alpha = TV(p_i, q_i)); target_logits holds gamma + 1 rows."""
+    lib = _lib.load()
+    B, gamma, V = draft_logits.shape
+    if alpha is None:
+        alpha = _alloc((B, gamma), torch.float64, draft_logits.device, stream)
+    ws = _workspace(acceptance_rate_workspace(B, gamma, V), draft_logits, workspace, stream)
+    _check(lib.s3r_acceptance_rate(
+        B, gamma, V, _dev(draft_logits, "draft_logits", torch.float32),
+        _dev(target_logits, "target_logits", torch.float32, (B, gamma + 1, V)), float(temperature),
+        _dev(alpha, "alpha", torch.float64, (B, gamma)), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+        _stream(stream)), "s3r_acceptance_rate")
+    return alpha

@@ -22,7 +22,8 @@ EXPORTS = [
     "s3r_page_bounds_update", "s3r_page_select", "s3r_sparse_draft_attn",
     "s3r_dense_verify_attn", "s3r_spec_sample", "s3r_status_string", "s3r_version",
     "s3r_sparse_draft_step_workspace", "s3r_sparse_draft_step", "s3r_sparse_draft_round",
-    "s3r_kv_commit",
+    "s3r_kv_commit", "s3r_draft_sample_workspace", "s3r_draft_sample",
+    "s3r_acceptance_rate_workspace", "s3r_acceptance_rate",
 ]
 
 
@@ -59,8 +60,8 @@ def load():
             "`python -m self_sparse_speculative_paged_amd.build` (there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(PagedKV)
-    vp, i32, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64,
-                             ctypes.c_float, ctypes.c_size_t)
+    vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                  ctypes.c_float, ctypes.c_size_t)
     sig = {
         "s3r_page_select_workspace": (sz, [P, i32]),
         "s3r_attn_workspace": (sz, [P, i32, i32]),
@@ -74,6 +75,10 @@ def load():
         "s3r_sparse_draft_round": (i32, [P, vp, vp, vp, i32, i32, f32, vp, vp, i32, vp, vp, sz, vp]),
         "s3r_kv_commit": (i32, [P, vp, vp, vp, i32, vp, vp]),
         "s3r_spec_sample": (i32, [i32, i32, i32, vp, vp, vp, f32, u64, u64, vp, vp, vp, sz, vp]),
+        "s3r_draft_sample_workspace": (sz, [i32, i32, i32]),
+        "s3r_draft_sample": (i32, [i32, i32, i32, vp, f32, u64, u64, i64, vp, vp, sz, vp]),
+        "s3r_acceptance_rate_workspace": (sz, [i32, i32, i32]),
+        "s3r_acceptance_rate": (i32, [i32, i32, i32, vp, vp, f32, vp, vp, sz, vp]),
         "s3r_status_string": (ctypes.c_char_p, [i32]),
         "s3r_version": (i32, []),
     }

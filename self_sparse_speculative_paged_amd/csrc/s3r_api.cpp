@@ -10,9 +10,11 @@
 
 namespace {
 
-constexpr int32_t kVersion = 200;  // 0.2.0: s3r_paged_kv gained num_phys_pages
+constexpr int32_t kVersion = 300;  // 0.3.0: the drafter's draws and the acceptance rate
 constexpr int32_t kMaxRows = 64;   // G * n_queries per kv head (4 MFMA row blocks)
 constexpr int32_t kMaxGamma = 16;
+// Largest grid of a sampling pass: one block per (sequence, row, 4096-token chunk).
+constexpr size_t kMaxBlocks = (size_t)1 << 31;
 
 // The kernels move K/V rows, bounds, queries, outputs and workspace through
 // 16-byte vector accesses.
@@ -498,6 +500,7 @@ s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
   if (draft_logits == nullptr || target_logits == nullptr || draft_tokens == nullptr ||
       out_tokens == nullptr || num_accepted == nullptr)
     return S3R_ERR_INVALID_ARGUMENT;
+  if (s3r::sample_blocks(num_seqs, 2 * gamma + 1, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::sample_workspace_bytes(num_seqs, gamma, vocab);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
   if (s3r::debug_checks_on())
@@ -519,6 +522,65 @@ s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
   a.seed = seed;
   a.offset = offset;
   return from_hip(s3r::launch_sample(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t s3r_draft_sample_workspace(int32_t num_seqs, int32_t n_rows, int32_t vocab) {
+  if (num_seqs < 1 || n_rows < 1 || vocab < 1) return 0;
+  return s3r::draft_sample_workspace_bytes(num_seqs, n_rows, vocab);
+}
+
+s3r_status s3r_draft_sample(int32_t num_seqs, int32_t n_rows, int32_t vocab, const float* logits,
+                            float temperature, uint64_t seed, uint64_t offset, int64_t first_slot,
+                            int32_t* tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 1 || n_rows < 1 || vocab < 1 || first_slot < 0) return S3R_ERR_INVALID_ARGUMENT;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARGUMENT;
+  if (logits == nullptr || tokens == nullptr) return S3R_ERR_INVALID_ARGUMENT;
+  if (s3r::sample_blocks(num_seqs, n_rows, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
+  const size_t need = s3r::draft_sample_workspace_bytes(num_seqs, n_rows, vocab);
+  if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  s3r::SampleArgs a{};
+  a.draft_logits = logits;
+  a.out_tokens = tokens;
+  a.workspace = workspace;
+  a.B = num_seqs;
+  a.rows = n_rows;
+  a.V = vocab;
+  a.n_chunks = s3r::sample_chunks(vocab);
+  a.first_slot = first_slot;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.offset = offset;
+  return from_hip(s3r::launch_draft_sample(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t s3r_acceptance_rate_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab) {
+  if (num_seqs < 1 || gamma < 1 || vocab < 1) return 0;
+  return s3r::acceptance_workspace_bytes(num_seqs, gamma, vocab);
+}
+
+s3r_status s3r_acceptance_rate(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                               const float* draft_logits, const float* target_logits,
+                               float temperature, double* alpha, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (num_seqs < 1 || gamma < 1 || vocab < 1) return S3R_ERR_INVALID_ARGUMENT;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARGUMENT;
+  if (draft_logits == nullptr || target_logits == nullptr || alpha == nullptr)
+    return S3R_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(alpha) & 7) != 0) return S3R_ERR_INVALID_ARGUMENT;
+  if (s3r::sample_blocks(num_seqs, 2 * gamma, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
+  const size_t need = s3r::acceptance_workspace_bytes(num_seqs, gamma, vocab);
+  if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  s3r::SampleArgs a{};
+  a.draft_logits = draft_logits;
+  a.target_logits = target_logits;
+  a.alpha = alpha;
+  a.workspace = workspace;
+  a.B = num_seqs;
+  a.gamma = gamma;
+  a.V = vocab;
+  a.n_chunks = s3r::sample_chunks(vocab);
+  a.temperature = temperature;
+  return from_hip(s3r::launch_acceptance(a, static_cast<hipStream_t>(stream)));
 }
 
 const char* s3r_status_string(s3r_status status) {

@@ -154,20 +154,32 @@ constexpr int fused_topk_keys(int waves) { return waves >= 8 ? 16 : 8; }
 constexpr int kWideTopkKeys = 32;
 
 struct SampleArgs {
-  const float* draft_logits;
-  const float* target_logits;
-  const int32_t* draft_tokens;
-  int32_t* out_tokens;
+  const float* draft_logits;   // [B][draft_rows][V]
+  const float* target_logits;  // [B][gamma + 1][V], or nullptr (the drafter's draws)
+  const int32_t* draft_tokens; // [B][gamma] (spec_sample only)
+  int32_t* out_tokens;         // spec_sample: [B][gamma + 1]; the drafter's draws: [B][rows]
   int32_t* num_accepted;
+  double* alpha;               // acceptance rate: [B][gamma]
   void* workspace;
   int32_t B, gamma, V, n_chunks;
+  int32_t rows;                // rows per sequence of the statistics pass (set by the launchers
+                               // except for the drafter's draws, where it is the caller's row count)
+  int32_t draft_rows;          // rows per sequence in draft_logits (set by the launchers)
+  int64_t first_slot;          // the drafter's draws: row r uses Philox slot first_slot + r
   float temperature;
   uint64_t seed, offset;
 };
 
 int32_t sample_chunks(int32_t vocab);
+// Blocks of the statistics pass over `rows` rows per sequence (the largest
+// grid of the sampling calls).
+size_t sample_blocks(int32_t B, int32_t rows, int32_t vocab);
 size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab);
+size_t draft_sample_workspace_bytes(int32_t B, int32_t rows, int32_t vocab);
+size_t acceptance_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+hipError_t launch_draft_sample(const SampleArgs& a, hipStream_t stream);
+hipError_t launch_acceptance(const SampleArgs& a, hipStream_t stream);
 
 // Checks of the device data the kernels trust, run when S3R_DEBUG is set
 // (s3r_debug.cpp). Each waits for the stream and returns INVALID_ARGUMENT on a

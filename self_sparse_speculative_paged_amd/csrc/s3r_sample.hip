@@ -1,25 +1,34 @@
-// Exact speculative sampling of one S3R round.
+// Exact speculative sampling of one S3R round, the drafter's own (direct)
+// sampling, and the acceptance rate.
 //
 // "S3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative Decoding",
 // Abstract: a dense check plus speculative sampling leaves the drafted output
-// distributed exactly as the dense policy's. The rule is
-// that of the speculative decoding / speculative sampling works the S3R
-// reference list cites: with p_i = softmax(target_i / T), q_i =
+// distributed exactly as the dense policy's, whereas sampling straight from
+// the sparse policy (no check) is the comparator the abstract finds unstable.
+// The rule is that of the speculative decoding / speculative sampling works
+// the S3R reference list cites: with p_i = softmax(target_i / T), q_i =
 // softmax(draft_i / T), accept draft x_i iff u_i < p_i(x_i) / q_i(x_i); at the
 // first rejection draw from norm(max(0, p_i - q_i)); if all gamma drafts are
-// accepted draw a bonus token from p_gamma.
+// accepted draw a bonus token from p_gamma. A draft is accepted with
+// probability alpha_i = sum_x min(p_i, q_i) = 1 - TV(p_i, q_i).
 //
-// Four passes, all deterministic (fixed-order reductions, no float atomics):
-//   stats:    per (sequence, row, 4096-token chunk) max and sum of exp, the sum
-//             accumulated in fp64;
-//   decide:   per sequence, fold the row statistics and run the accept scan;
-//   residual: per (sequence, chunk) sum the chunk's residual (or bonus)
-//             weights in fp64, per 16-token run and per chunk;
-//   finalize: per sequence, locate the chunk holding u * sum(w), then the
-//             16-token run inside it, then the token, each by an ordered wave
-//             scan; write the round's tokens.
+// Every pass is deterministic (fixed-order reductions, no float atomics):
+//   stats:    per (sequence, row, 4096-token chunk) max and sum of
+//             2^((x - max) log2(e) / T), the sum folded in fp64; the block that
+//             holds a row's drafted token also keeps that token's logit;
+//   residual: per (sequence, chunk), every block first folds the row
+//             statistics and runs the accept scan itself (all blocks of a
+//             sequence reach the same decision), then sums the chunk's
+//             residual (or bonus) weights in fp64;
+//   finalize: per sequence, locate the chunk holding u * sum(w) by an ordered
+//             wave scan over the chunk sums, then the token inside it by an
+//             ordered block scan over the chunk's recomputed weights.
+// The drafter's draws (stats, then one draw block per row) and the acceptance
+// rate (stats, per-chunk sums of min(p, q), an ordered fold) reuse the pieces.
 // Uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) at key
 // (seed, 0), counter (offset, b, slot, stream); u = (word0 >> 11) * 2^-53.
+// Streams: 0 accept tests, 1 residual and bonus draws, 2 the drafter's draws.
+#include <limits.h>
 #include <math.h>
 
 #include "s3r_common.h"
@@ -30,7 +39,10 @@ namespace {
 
 constexpr int kChunk = 4096;
 constexpr int kThreads = 256;
-constexpr int kPerThread = kChunk / kThreads;  // also the tokens of one residual run
+constexpr int kWaves = kThreads / 64;
+constexpr int kPerThread = kChunk / kThreads;  // tokens per thread of a chunk
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr double kLog2e = 1.4426950408889634;
 
 // Philox4x64-10 round multipliers and Weyl key increments (Salmon et al.).
 constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
@@ -57,290 +69,104 @@ __device__ double philox_uniform(uint64_t seed, uint64_t offset, uint64_t b, uin
   return (double)(x0 >> 11) * 0x1.0p-53;
 }
 
-struct Layout {
-  double* sum;     // [B][R][C] chunk sum of exp((x - chunk max) / T)
-  double* wsum;    // [B][C] chunk sum of the residual/bonus weights
-  double* psum;    // [B][C] chunk sum of the target row's probabilities
-  double* wrun;    // [B][C][kThreads] the same over each 16-token run
-  double* prun;    // [B][C][kThreads]
-  double* iz;      // [B][R] 1 / row normaliser, as the residual pass used it
-  float* cmax;     // [B][R][C] chunk max logit
-  float* rmax;     // [B][R] row max logit
-  int* nacc;       // [B] accepted drafts
+// What the final draw of a sequence needs from its accept scan.
+struct Decision {
+  double izt, izd;  // 1 / normaliser of the target and draft rows of the draw
+  float mt, md;     // their max logits
+  int32_t n;        // accepted drafts
+  int32_t pad;
 };
 
-__host__ __device__ inline Layout layout_of(void* ws, int B, int gamma, int C) {
-  const size_t R = 2 * (size_t)gamma + 1;
+struct Layout {
+  double* csum;    // [B][R][C] chunk sum of 2^((x - chunk max) * log2(e) / T)
+  double* wsum;    // [B][C] chunk mass of the final draw's weights
+  double* psum;    // [B][C] chunk mass of the target row (the zero-residual fallback)
+  double* apart;   // [B][gamma][C] chunk sums of min(p, q)
+  Decision* dec;   // [B]
+  float* cmax;     // [B][R][C] chunk max logit
+  float* probe;    // [B][R] logit at the row's drafted token
+};
+
+enum Pass { kSpecPass = 0, kDrawPass = 1, kAlphaPass = 2 };
+
+// Carves the workspace (base == nullptr: sizing only); returns its size.
+__host__ __device__ inline size_t layout_of(void* base, int pass, size_t B, size_t R, size_t C,
+                                            size_t gamma, Layout* L) {
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return q;
+  };
+  Layout l{};
+  l.csum = reinterpret_cast<double*>(take(sizeof(double) * B * R * C));
+  l.cmax = reinterpret_cast<float*>(take(sizeof(float) * B * R * C));
+  if (pass == kSpecPass) {
+    l.probe = reinterpret_cast<float*>(take(sizeof(float) * B * R));
+    l.wsum = reinterpret_cast<double*>(take(sizeof(double) * B * C));
+    l.psum = reinterpret_cast<double*>(take(sizeof(double) * B * C));
+    l.dec = reinterpret_cast<Decision*>(take(sizeof(Decision) * B));
+  }
+  if (pass == kAlphaPass) l.apart = reinterpret_cast<double*>(take(sizeof(double) * B * gamma * C));
+  if (L) *L = l;
+  return off;
+}
+
+__device__ __forceinline__ Layout layout(const SampleArgs& a, int pass) {
   Layout l;
-  char* p = static_cast<char*>(ws);
-  l.sum = reinterpret_cast<double*>(p);
-  p += sizeof(double) * B * R * C;
-  l.wsum = reinterpret_cast<double*>(p);
-  p += sizeof(double) * B * C;
-  l.psum = reinterpret_cast<double*>(p);
-  p += sizeof(double) * B * C;
-  l.wrun = reinterpret_cast<double*>(p);
-  p += sizeof(double) * B * C * kThreads;
-  l.prun = reinterpret_cast<double*>(p);
-  p += sizeof(double) * B * C * kThreads;
-  l.iz = reinterpret_cast<double*>(p);
-  p += sizeof(double) * B * R;
-  l.cmax = reinterpret_cast<float*>(p);
-  p += sizeof(float) * B * R * C;
-  l.rmax = reinterpret_cast<float*>(p);
-  p += sizeof(float) * B * R;
-  l.nacc = reinterpret_cast<int*>(p);
+  layout_of(a.workspace, pass, a.B, a.rows, a.n_chunks, a.gamma, &l);
   return l;
 }
 
-// Row r of sequence b: draft rows 0..gamma-1, target rows gamma..2*gamma.
+// Row r of sequence b in the statistics pass: rows 0 .. draft_rows - 1 of the
+// draft logits, then the rows of the target logits.
 __device__ __forceinline__ const float* row_ptr(const SampleArgs& a, int b, int r) {
-  return r < a.gamma ? a.draft_logits + ((size_t)b * a.gamma + r) * a.V
-                     : a.target_logits + ((size_t)b * (a.gamma + 1) + (r - a.gamma)) * a.V;
+  return r < a.draft_rows ? a.draft_logits + ((size_t)b * a.draft_rows + r) * a.V
+                          : a.target_logits + ((size_t)b * (a.gamma + 1) + (r - a.draft_rows)) * a.V;
 }
 
-// exp((x - m) / T) as 2^((x - m) * log2(e) / T): one v_exp_f32 per element.
-// The argument's fp32 rounding moves each term by ~1e-7 relative at the
-// magnitudes that carry mass; the sums are accumulated in fp64.
-__device__ __forceinline__ float scaled_exp(float x, float m, float c_log2) {
-  return __builtin_amdgcn_exp2f((x - m) * c_log2);
-}
-
-template <typename T>
-__device__ T block_reduce_sum(T v, T* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) v += __shfl_xor(v, x, 64);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  const T t = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return t;
-}
-
-__device__ float block_reduce_max(float v, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) v = fmaxf(v, __shfl_xor(v, x, 64));
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return t;
-}
-
-__global__ __launch_bounds__(kThreads) void stats_kernel(SampleArgs a) {
-  __shared__ float redf[4];
-  __shared__ double redd[4];
-  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const float* row = row_ptr(a, b, r);
-  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
-  float x[kPerThread];
-  float m = -__builtin_huge_valf();
-  // Thread t owns tokens lo + 4*(t + 256*k) .. +3 (16-byte loads when the row
-  // is 16-byte aligned, scalar loads otherwise).
-  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+// The chunk's tokens, coalesced: load k of thread t holds tokens
+// lo + 4 * (t + kThreads * k) .. + 3 (16-byte loads when the row is 16-byte
+// aligned, scalar loads otherwise). Tokens past hi read -inf.
+__device__ __forceinline__ void load_strided(const float* row, int lo, int hi, float (&x)[kPerThread]) {
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
 #pragma unroll
   for (int k = 0; k < kPerThread / 4; ++k) {
-    const int t = lo + 4 * (threadIdx.x + kThreads * k);
+    const int t = lo + 4 * ((int)threadIdx.x + kThreads * k);
     if (vec && t + 3 < hi) {
       const f32x4 v = load_nt16<f32x4>(row + t);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[4 * k + e] = v[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * k + e] = t + e < hi ? row[t + e] : -__builtin_huge_valf();
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m = fmaxf(m, x[4 * k + e]);
-  }
-  m = block_reduce_max(m, redf);
-  const float c_log2 = 1.4426950408889634f / a.temperature;
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k) s += scaled_exp(x[k], m, c_log2);  // -inf pads give 0
-  const double sd = block_reduce_sum<double>((double)s, redd);
-  if (threadIdx.x == 0) {
-    const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-    const size_t idx = ((size_t)b * (2 * a.gamma + 1) + r) * a.n_chunks + c;
-    L.sum[idx] = sd;
-    L.cmax[idx] = m;
-  }
-}
-
-// Per-block view of one sequence's round: row normalisers and the accept scan.
-struct Round {
-  float M[2 * 16 + 1];    // row max logit
-  double Z[2 * 16 + 1];   // sum over the row of 2^((x - M) * log2(e) / T)
-  double iZ[2 * 16 + 1];
-  int accept[16];
-  int n;                  // accepted drafts
-};
-
-// Threads r < 2*gamma+1 fold row r's chunk statistics in chunk order; threads
-// i < gamma then decide draft i (gathered logits, fp64 ratio, Philox uniform)
-// and thread 0 takes the first rejection. Identical in every calling block.
-__device__ void round_decision(const SampleArgs& a, int b, Round& rd) {
-  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-  const int R = 2 * a.gamma + 1;
-  const double c_log2 = 1.4426950408889634 / (double)a.temperature;
-  // Wave w folds rows w, w+4, ...: lane l takes chunks l, l+64, ... and the
-  // lanes are combined by a fixed butterfly (deterministic). The loads of all
-  // the wave's rows are issued before any is folded.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kRowsPerWave = (2 * 16 + 1 + kThreads / 64 - 1) / (kThreads / 64);
-  for (int c0 = 0; c0 == 0 || c0 < a.n_chunks; c0 += 64) {
-    float cm[kRowsPerWave];
-    double cs[kRowsPerWave];
-#pragma unroll
-    for (int k = 0; k < kRowsPerWave; ++k) {
-      const int r = wave + (kThreads / 64) * k;
-      const int c = c0 + lane;
-      const bool ok = r < R && c < a.n_chunks;
-      const size_t idx = ((size_t)b * R + (ok ? r : 0)) * a.n_chunks + (ok ? c : 0);
-      cm[k] = ok ? L.cmax[idx] : -__builtin_huge_valf();
-      cs[k] = ok ? L.sum[idx] : 0.0;
-    }
-#pragma unroll
-    for (int k = 0; k < kRowsPerWave; ++k) {
-      const int r = wave + (kThreads / 64) * k;
-      if (r >= R) break;
-      float M = cm[k];
-#pragma unroll
-      for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
-      double Z = cs[k] > 0.0 ? cs[k] * exp2(((double)cm[k] - (double)M) * c_log2) : 0.0;
-#pragma unroll
-      for (int x = 32; x >= 1; x >>= 1) Z += __shfl_xor(Z, x, 64);
-      if (lane == 0) {
-        if (c0 == 0) {
-          rd.M[r] = M;
-          rd.Z[r] = Z;
-        } else {  // more than 64 chunks: fold this pass into the running values
-          // A side without mass adds nothing; rescaling it would form
-          // 0 * 2^(-inf - -inf) = NaN when every token so far is masked.
-          const float Mn = fmaxf(rd.M[r], M);
-          const double zr = rd.Z[r] > 0.0 ? rd.Z[r] * exp2(((double)rd.M[r] - Mn) * c_log2) : 0.0;
-          const double zp = Z > 0.0 ? Z * exp2(((double)M - Mn) * c_log2) : 0.0;
-          rd.Z[r] = zr + zp;
-          rd.M[r] = Mn;
-        }
-        rd.iZ[r] = 1.0 / rd.Z[r];
-      }
+      for (int e = 0; e < 4; ++e) x[4 * k + e] = t + e < hi ? row[t + e] : kNegInf;
     }
   }
-  __syncthreads();
-  const int i = threadIdx.x;
-  if (i < a.gamma) {
-    const int x = a.draft_tokens[(size_t)b * a.gamma + i];
-    const double lt = row_ptr(a, b, a.gamma + i)[x];
-    const double ld = row_ptr(a, b, i)[x];
-    const double p = exp2((lt - (double)rd.M[a.gamma + i]) * c_log2) / rd.Z[a.gamma + i];
-    const double q = exp2((ld - (double)rd.M[i]) * c_log2) / rd.Z[i];
-    const double u = philox_uniform(a.seed, a.offset, b, i, 0);
-    rd.accept[i] = q > 0.0 ? (u < p / q) : (p > 0.0);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < a.gamma && rd.accept[n]) ++n;
-    rd.n = n;
-  }
-  __syncthreads();
 }
 
-// One block per sequence: fold the row statistics, run the accept scan and
-// store (row max, 1/normaliser, accepted count) for the two passes that follow.
-__global__ __launch_bounds__(kThreads) void decide_kernel(SampleArgs a) {
-  __shared__ Round rd;
-  const int b = blockIdx.x;
-  round_decision(a, b, rd);
-  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-  const int R = 2 * a.gamma + 1;
-  if (threadIdx.x < (unsigned)R) {
-    L.rmax[(size_t)b * R + threadIdx.x] = rd.M[threadIdx.x];
-    L.iz[(size_t)b * R + threadIdx.x] = rd.iZ[threadIdx.x];
-  }
-  if (threadIdx.x == 0) L.nacc[b] = rd.n;
-}
-
-__device__ __forceinline__ void load_decision(const SampleArgs& a, int b, Round& rd) {
-  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-  const int R = 2 * a.gamma + 1;
-  if (threadIdx.x < (unsigned)R) {
-    rd.M[threadIdx.x] = L.rmax[(size_t)b * R + threadIdx.x];
-    rd.iZ[threadIdx.x] = L.iz[(size_t)b * R + threadIdx.x];
-  }
-  if (threadIdx.x == 0) rd.n = L.nacc[b];
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
-  __shared__ Round rd;
-  __shared__ double redd[4];
-  const int c = blockIdx.x, b = blockIdx.y;
-  load_decision(a, b, rd);
-  const float c_log2 = 1.4426950408889634f / a.temperature;
-  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
-  const int tr = a.gamma + rd.n, dr = rd.n < a.gamma ? rd.n : tr;
-  const float* trow = row_ptr(a, b, tr);
-  const float* drow = row_ptr(a, b, dr);
-  // Coalesced as in the stats pass: load k of thread t covers tokens
-  // lo + 4 * (t + kThreads * k) .. + 3. A run of 16 consecutive tokens is then
-  // four adjacent lanes of one load, folded by a fixed quad reduction.
-  const bool vec = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15) == 0;
-  float xt[kPerThread], xd[kPerThread];
+// The same tokens, each thread owning kPerThread consecutive ones: thread t
+// holds lo + kPerThread * t .. + kPerThread - 1 in token order.
+__device__ __forceinline__ void load_contiguous(const float* row, int lo, int hi, float (&x)[kPerThread]) {
+  const int t0 = lo + kPerThread * (int)threadIdx.x;
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0 && t0 + kPerThread <= hi;
 #pragma unroll
   for (int k = 0; k < kPerThread / 4; ++k) {
-    const int t = lo + 4 * (threadIdx.x + kThreads * k);
-    if (vec && t + 3 < hi) {
-      const f32x4 vt = load_nt16<f32x4>(trow + t);
-      const f32x4 vd = load_nt16<f32x4>(drow + t);
+    if (vec) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + t0 + 4 * k);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xt[4 * k + e] = vt[e];
-        xd[4 * k + e] = vd[e];
-      }
+      for (int e = 0; e < 4; ++e) x[4 * k + e] = v[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xt[4 * k + e] = t + e < hi ? trow[t + e] : -__builtin_huge_valf();
-        xd[4 * k + e] = t + e < hi ? drow[t + e] : -__builtin_huge_valf();
-      }
+      for (int e = 0; e < 4; ++e) x[4 * k + e] = t0 + 4 * k + e < hi ? row[t0 + 4 * k + e] : kNegInf;
     }
   }
-  const bool bonus = rd.n == a.gamma;
-  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
-  double* wrun = L.wrun + ((size_t)b * a.n_chunks + c) * kThreads;
-  double* prun = L.prun + ((size_t)b * a.n_chunks + c) * kThreads;
-  double w = 0.0, ps = 0.0;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
-  for (int k = 0; k < kPerThread / 4; ++k) {
-    double wk = 0.0, pk = 0.0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {  // token order
-      const double p = (double)scaled_exp(xt[4 * k + e], rd.M[tr], c_log2) * rd.iZ[tr];
-      const double q = bonus ? 0.0 : (double)scaled_exp(xd[4 * k + e], rd.M[dr], c_log2) * rd.iZ[dr];
-      wk += p > q ? p - q : 0.0;
-      pk += p;
-    }
-    w += wk;
-    ps += pk;
-    wk += __shfl_xor(wk, 1, 64);
-    pk += __shfl_xor(pk, 1, 64);
-    wk += __shfl_xor(wk, 2, 64);
-    pk += __shfl_xor(pk, 2, 64);
-    if ((threadIdx.x & 3) == 0) {
-      const int r = (kThreads / 4) * k + threadIdx.x / 4;  // run index inside the chunk
-      wrun[r] = wk;
-      prun[r] = pk;
-    }
-  }
-  w = block_reduce_sum<double>(w, redd);
-  ps = block_reduce_sum<double>(ps, redd);
-  if (threadIdx.x == 0) {
-    L.wsum[(size_t)b * a.n_chunks + c] = w;
-    L.psum[(size_t)b * a.n_chunks + c] = ps;
-  }
+  for (int x = 32; x >= 1; x >>= 1) v += __shfl_xor(v, x, 64);
+  return v;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order.
@@ -354,135 +180,470 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
   return v;
 }
 
-// One wave per sequence draws the round's last token by inverse CDF over the
-// residual (or bonus) weights: lanes own contiguous chunk ranges, then
-// contiguous 64-token runs of the chosen chunk; running sums are ordered wave
-// scans, so the draw is deterministic.
-constexpr int kFinalizeLanes = 64;
+// The exclusive prefix from an inclusive one: lane l gets lane l - 1's value,
+// lane 0 gets 0. The shuffle runs on every lane: a lane that reads from a lane
+// left out of the shuffle would read 0.
+__device__ __forceinline__ double wave_exclusive_from(double incl) {
+  const double up = __shfl_up(incl, 1, 64);
+  return (threadIdx.x & 63) == 0 ? 0.0 : up;
+}
 
-__global__ __launch_bounds__(kFinalizeLanes) void finalize_kernel(SampleArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const Layout L = layout_of(a.workspace, a.B, a.gamma, a.n_chunks);
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) v = min(v, __shfl_xor(v, x, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) v = max(v, __shfl_xor(v, x, 64));
+  return v;
+}
+
+// Max M and Z = sum_c csum_c * 2^((cmax_c - M) * log2(e) / T) of one row's
+// chunk statistics, folded by one wave in a fixed order (lane l takes chunks
+// l, l + 64, ..., then a butterfly). A chunk without mass adds nothing (its
+// rescale would be 0 * 2^(-inf - -inf)). Every lane returns the result.
+__device__ __forceinline__ void fold_row(const float* cmax, const double* csum, int C, double cl,
+                                         float& M, double& Z) {
+  const int lane = threadIdx.x & 63;
+  float m = kNegInf;
+  for (int c = lane; c < C; c += 64) m = fmaxf(m, cmax[c]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
+  double z = 0.0;
+  for (int c = lane; c < C; c += 64) {
+    const double s = csum[c];
+    if (s > 0.0) z += s * exp2(((double)cmax[c] - (double)m) * cl);
+  }
+  M = m;
+  Z = wave_sum_f64(z);
+}
+
+// ---------------------------------------------------------------------------
+// Statistics pass: one block per (sequence, row, chunk).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void stats_kernel(SampleArgs a, int pass) {
+  __shared__ float wm[kWaves];
+  __shared__ double ws[kWaves];
+  const int C = a.n_chunks;
+  const int c = blockIdx.x % C;
+  const int br = blockIdx.x / C;
+  const int r = br % a.rows, b = br / a.rows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
+  // The drafted token whose logit this row's accept test reads (spec_sample).
+  int tok = -1;
+  if (pass == kSpecPass && r < 2 * a.gamma) tok = a.draft_tokens[(size_t)b * a.gamma + (r < a.gamma ? r : r - a.gamma)];
+  float x[kPerThread];
+  load_strided(row_ptr(a, b, r), lo, hi, x);
+  const Layout L = layout(a, pass);
+  if (tok >= lo && tok < hi) {
+    const int rel = tok - lo;
+    if ((int)threadIdx.x == ((rel >> 2) & (kThreads - 1))) {
+      const int j = 4 * (rel / (4 * kThreads)) + (rel & 3);
+      float v = x[0];
+#pragma unroll
+      for (int e = 1; e < kPerThread; ++e) v = e == j ? x[e] : v;
+      L.probe[(size_t)b * a.rows + r] = v;
+    }
+  }
+  // Wave max, then every term against it (one rounding each), summed in fp32
+  // per thread and fp64 across the wave; the four wave partials are merged by
+  // thread 0 in wave order.
+  float m = x[0];
+#pragma unroll
+  for (int e = 1; e < kPerThread; ++e) m = fmaxf(m, x[e]);
+  m = wave_xor_max<1, 32>(m);
+  const float cl = (float)kLog2e / a.temperature;
+  float s = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * cl);
+  }
+  const double sd = wave_sum_f64((double)s);
+  if (lane == 0) {
+    wm[wave] = m;
+    ws[wave] = sd;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = wm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
+    double S = 0.0;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (wm[w] != kNegInf) S += ws[w] * (double)__builtin_amdgcn_exp2f((wm[w] - M) * cl);
+    }
+    const size_t idx = ((size_t)b * a.rows + r) * C + c;
+    L.cmax[idx] = M;
+    L.csum[idx] = S;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The accept scan, in every block of a sequence: fold the round's 2 gamma + 1
+// row statistics (wave w folds rows w, w + 4, ...), then test the gamma drafts
+// in parallel (lane i of each wave tests draft i, so every wave reaches the
+// decision without another barrier).
+// ---------------------------------------------------------------------------
+struct RoundRows {
+  float M[2 * 16 + 1];
+  double Z[2 * 16 + 1];
+};
+
+__device__ int round_decision(const SampleArgs& a, const Layout& L, int b, RoundRows& rr) {
+  const int R = 2 * a.gamma + 1, C = a.n_chunks;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double cl = kLog2e / (double)a.temperature;
+  for (int r = wave; r < R; r += kWaves) {
+    float M;
+    double Z;
+    const size_t base = ((size_t)b * R + r) * C;
+    fold_row(L.cmax + base, L.csum + base, C, cl, M, Z);
+    if (lane == 0) {
+      rr.M[r] = M;
+      rr.Z[r] = Z;
+    }
+  }
+  __syncthreads();
+  bool reject = false;
+  if (lane < a.gamma) {
+    const int i = lane;
+    const double lt = L.probe[(size_t)b * R + a.gamma + i];
+    const double ld = L.probe[(size_t)b * R + i];
+    const double p = exp2((lt - (double)rr.M[a.gamma + i]) * cl) / rr.Z[a.gamma + i];
+    const double q = exp2((ld - (double)rr.M[i]) * cl) / rr.Z[i];
+    const double u = philox_uniform(a.seed, a.offset, b, i, 0);
+    reject = !(q > 0.0 ? (u < p / q) : (p > 0.0));
+  }
+  const uint64_t rej = __ballot(reject);
+  return rej ? (int)__builtin_ctzll(rej) : a.gamma;
+}
+
+// 2^v for a draw weight: the hardware fp32 exp2, or the fp64 exp2 where that
+// underflows, so a finite logit never gets a zero weight while its chunk's
+// statistics (folded in fp64) give the chunk mass.
+__device__ __forceinline__ double weight_exp2(float v) {
+  const float e = __builtin_amdgcn_exp2f(v);
+  return (e != 0.f || v == kNegInf) ? (double)e : exp2((double)v);
+}
+
+// Per-thread weights of the final draw from the two rows' logits.
+struct DrawWeights {
+  float mt, md;
+  double izt, izd;
+  float cl;
+  int mode;  // 0: max(0, p - q); 1: p
+  __device__ __forceinline__ double p_of(float xt) const { return weight_exp2((xt - mt) * cl) * izt; }
+  __device__ __forceinline__ double operator()(float xt, float xd) const {
+    const double p = p_of(xt);
+    if (mode == 1) return p;
+    const double q = weight_exp2((xd - md) * cl) * izd;
+    return p > q ? p - q : 0.0;
+  }
+};
+
+// Fixed-order block sum of v into thread 0's return value (others: partial).
+__device__ __forceinline__ double block_sum_to_thread0(double v, double* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_f64(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += red[w];
+  }
+  return t;
+}
+
+// One block per (sequence, chunk): the accept scan, then the chunk's mass of
+// the final draw's weights max(0, p - q) (p for the bonus), and of p.
+__global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
+  __shared__ RoundRows rr;
+  __shared__ double red[2][kWaves];
+  const int C = a.n_chunks;
+  const int c = blockIdx.x % C, b = blockIdx.x / C;
   const int R = 2 * a.gamma + 1;
-  const int n = L.nacc[b];
+  const Layout L = layout(a, kSpecPass);
+  const int n = round_decision(a, L, b, rr);
   const int tr = a.gamma + n, dr = n < a.gamma ? n : tr;
-  const float Mt = L.rmax[(size_t)b * R + tr], Md = L.rmax[(size_t)b * R + dr];
-  const double iZt = L.iz[(size_t)b * R + tr], iZd = L.iz[(size_t)b * R + dr];
   const bool bonus = n == a.gamma;
-  const double u = philox_uniform(a.seed, a.offset, b, n, 1);
+  const double izt = 1.0 / rr.Z[tr], izd = 1.0 / rr.Z[dr];
+  if (c == 0 && threadIdx.x == 0) {
+    Decision d;
+    d.izt = izt;
+    d.izd = izd;
+    d.mt = rr.M[tr];
+    d.md = rr.M[dr];
+    d.n = n;
+    d.pad = 0;
+    L.dec[b] = d;
+  }
+  const double cl = kLog2e / (double)a.temperature;
+  if (bonus) {
+    // w = p: the chunk's mass follows from its statistics, no logits read.
+    if (threadIdx.x == 0) {
+      const size_t idx = ((size_t)b * R + tr) * C + c;
+      const double s = L.csum[idx];
+      const double mass = s > 0.0 ? s * exp2(((double)L.cmax[idx] - (double)rr.M[tr]) * cl) * izt : 0.0;
+      L.wsum[(size_t)b * C + c] = mass;
+      L.psum[(size_t)b * C + c] = mass;
+    }
+    return;
+  }
+  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
+  float xt[kPerThread], xd[kPerThread];
+  load_strided(row_ptr(a, b, tr), lo, hi, xt);
+  load_strided(row_ptr(a, b, dr), lo, hi, xd);
+  DrawWeights wf{rr.M[tr], rr.M[dr], izt, izd, (float)cl, 0};
+  double w = 0.0, ps = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    w += wf(xt[e], xd[e]);
+    ps += wf.p_of(xt[e]);
+  }
+  w = block_sum_to_thread0(w, red[0]);
+  ps = block_sum_to_thread0(ps, red[1]);
+  if (threadIdx.x == 0) {
+    L.wsum[(size_t)b * C + c] = w;
+    L.psum[(size_t)b * C + c] = ps;
+  }
+}
 
-  // Chunk level.
-  const int per = (a.n_chunks + 63) / 64;
-  const int c0 = min(a.n_chunks, lane * per), c1 = min(a.n_chunks, c0 + per);
-  double own_w = 0.0, own_p = 0.0;
+// ---------------------------------------------------------------------------
+// Locating u * total: first over the chunk masses (ordered wave scan, lanes
+// owning contiguous chunk ranges), then inside the chosen chunk.
+// ---------------------------------------------------------------------------
+struct ChunkPick {
+  int chunk;
+  double before;  // mass of the chunks before it
+  double target;  // u * total
+  double total;
+  bool fallback;  // rounding left no crossing: the last chunk with mass
+};
+
+template <class Mass>
+__device__ ChunkPick pick_chunk(int C, double u, const Mass& mass) {
+  const int lane = threadIdx.x & 63;
+  const int per = (C + 63) / 64;
+  const int c0 = min(C, lane * per), c1 = min(C, c0 + per);
+  double own = 0.0;
   int last_pos = -1;
   for (int c = c0; c < c1; ++c) {
-    const double w = L.wsum[(size_t)b * a.n_chunks + c];
-    own_w += w;
-    own_p += L.psum[(size_t)b * a.n_chunks + c];
+    const double w = mass(c);
+    own += w;
     if (w > 0.0) last_pos = c;
   }
-  double incl = wave_inclusive_scan(own_w);
-  double total = __shfl(incl, 63, 64);
-  const bool use_p = !(total > 0.0);  // residual without mass (rounding only): draw from p
-  if (use_p) {
-    incl = wave_inclusive_scan(own_p);
-    total = __shfl(incl, 63, 64);
-  }
-  const double target = u * total;
-  int chunk = 0x7fffffff;
-  double before = 0.0;
-  {
-    double run = incl - (use_p ? own_p : own_w);
-    for (int c = c0; c < c1; ++c) {
-      const double w = use_p ? L.psum[(size_t)b * a.n_chunks + c] : L.wsum[(size_t)b * a.n_chunks + c];
-      if (use_p && w > 0.0) last_pos = c;
-      if (run + w > target) {
-        chunk = c;
-        before = run;
-        break;
-      }
-      run += w;
+  const double incl = wave_inclusive_scan(own);
+  const double excl = wave_exclusive_from(incl);
+  ChunkPick pk;
+  pk.total = __shfl(incl, 63, 64);
+  pk.target = u * pk.total;
+  int chunk = INT_MAX;
+  double before = 0.0, run = excl;
+  for (int c = c0; c < c1; ++c) {
+    const double w = mass(c);
+    if (run + w > pk.target) {
+      chunk = c;
+      before = run;
+      break;
     }
+    run += w;
   }
-  // The first crossing chunk over the wave (or, if rounding left none, the
-  // last chunk with mass).
-  int best = chunk;
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) best = min(best, __shfl_xor(best, x, 64));
-  const bool fallback = best == 0x7fffffff;
-  if (fallback) {
-    int lp = last_pos;
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) lp = max(lp, __shfl_xor(lp, x, 64));
-    best = max(lp, 0);
-  }
-  const unsigned long long owner = __ballot(chunk == best);
-  const double base = fallback ? 0.0 : __shfl(before, owner ? __ffsll(owner) - 1 : 0, 64);
+  int best = wave_min_i(chunk);
+  pk.fallback = best == INT_MAX;
+  if (pk.fallback) best = max(wave_max_i(last_pos), 0);
+  const uint64_t owner = __ballot(chunk == best);
+  const double owner_before = __shfl(before, owner ? (int)__builtin_ctzll(owner) : 0, 64);
+  pk.before = pk.fallback ? 0.0 : owner_before;
+  pk.chunk = best;
+  return pk;
+}
 
-  // Run level inside the chosen chunk: lane l scans runs 4l .. 4l+3. Rounding
-  // can leave the target past the runs' total; then (as for chunks) the last
-  // run with mass is taken.
-  const double* runs = (use_p ? L.prun : L.wrun) + ((size_t)b * a.n_chunks + best) * kThreads;
-  double rw[kThreads / 64], rown = 0.0;
+struct DrawShared {
+  double wtot[kWaves];
+  int first[kWaves];
+  int last[kWaves];
+  int token;
+};
+
+// The token of chunk [lo, hi) at which before + the running sum of w passes
+// target, tokens in ascending order (thread t owns kPerThread consecutive
+// ones; an ordered block scan gives each thread its start). If none passes,
+// which only rounding between the two levels allows, or `fallback` is set,
+// the chunk's last token with w > 0. Every thread calls it and gets the token.
+template <class W>
+__device__ int draw_in_chunk(const float* trow, const float* drow, int lo, int hi, double before,
+                             double target, bool fallback, const W& wfn, DrawShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float xt[kPerThread], xd[kPerThread];
+  load_contiguous(trow, lo, hi, xt);
+  if (drow) {
+    load_contiguous(drow, lo, hi, xd);
+  } else {
 #pragma unroll
-  for (int e = 0; e < kThreads / 64; ++e) {
-    rw[e] = runs[(kThreads / 64) * lane + e];
-    rown += rw[e];
+    for (int e = 0; e < kPerThread; ++e) xd[e] = kNegInf;
   }
-  const double rincl = wave_inclusive_scan(rown);
-  double rrun = base + rincl - rown;
-  int rfirst = 0x7fffffff, rlast = -1;
-  double rbefore = 0.0;
+  const int t0 = lo + kPerThread * (int)threadIdx.x;
+  double w[kPerThread], own = 0.0;
+  int last = -1;
 #pragma unroll
-  for (int e = 0; e < kThreads / 64; ++e) {
-    const int r = (kThreads / 64) * lane + e;
-    if (rw[e] > 0.0) rlast = r;
-    if (rfirst == 0x7fffffff && !fallback && rrun + rw[e] > target) {
-      rfirst = r;
-      rbefore = rrun;
+  for (int e = 0; e < kPerThread; ++e) {
+    w[e] = t0 + e < hi ? wfn(xt[e], xd[e]) : 0.0;
+    own += w[e];
+    if (w[e] > 0.0) last = t0 + e;
+  }
+  const double incl = wave_inclusive_scan(own);
+  const double wexcl = wave_exclusive_from(incl);
+  if (lane == 63) sh.wtot[wave] = incl;
+  last = wave_max_i(last);
+  if (lane == 0) sh.last[wave] = last;
+  __syncthreads();
+  double run = before;
+  for (int v = 0; v < wave; ++v) run += sh.wtot[v];
+  run += wexcl;
+  const bool cross = !fallback && run + own > target;
+  const uint64_t cm = __ballot(cross);
+  if (lane == 0) sh.first[wave] = cm ? wave * 64 + (int)__builtin_ctzll(cm) : INT_MAX;
+  __syncthreads();
+  int first = INT_MAX, block_last = -1;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    first = min(first, sh.first[v]);
+    block_last = max(block_last, sh.last[v]);
+  }
+  if (first == INT_MAX) return block_last;  // uniform: no thread crossed
+  if ((int)threadIdx.x == first) {
+    int tok = -1;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (tok < 0 && run + w[e] > target) tok = t0 + e;
+      run += w[e];
     }
-    rrun += rw[e];
+    sh.token = tok >= 0 ? tok : last;  // rounding inside the run: its last token with mass
   }
-  int rsel = rfirst;
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) rsel = min(rsel, __shfl_xor(rsel, x, 64));
-  const bool rfall = rsel == 0x7fffffff;
-  if (rfall) {
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) rlast = max(rlast, __shfl_xor(rlast, x, 64));
-    rsel = max(rlast, 0);
-  }
-  const unsigned long long rowner = __ballot(rfirst == rsel);
-  const double rbase = rfall ? 0.0 : __shfl(rbefore, rowner ? __ffsll(rowner) - 1 : 0, 64);
+  __syncthreads();
+  return sh.token;
+}
 
-  // Token level: lanes 0..15 take the run's 16 tokens.
-  const float c_log2 = 1.4426950408889634f / a.temperature;
-  const int lo = best * kChunk, hi = min(a.V, lo + kChunk);
-  const int t = lo + kPerThread * rsel + (lane & (kPerThread - 1));
-  const bool mine = lane < kPerThread && t < hi;
-  const float* trow = row_ptr(a, b, tr);
-  const float* drow = row_ptr(a, b, dr);
-  const float xt = mine ? trow[t] : -__builtin_huge_valf();
-  const float xd = mine ? drow[t] : -__builtin_huge_valf();
-  const double p = (double)scaled_exp(xt, Mt, c_log2) * iZt;
-  const double q = bonus ? 0.0 : (double)scaled_exp(xd, Md, c_log2) * iZd;
-  const double w = mine ? (use_p ? p : (p > q ? p - q : 0.0)) : 0.0;
-  const double tincl = wave_inclusive_scan(w);
-  const bool hit = mine && !fallback && !rfall && rbase + tincl > target;
-  int first = hit ? t : 0x7fffffff;
-  int last = mine && w > 0.0 ? t : -1;
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) {
-    first = min(first, __shfl_xor(first, x, 64));
-    last = max(last, __shfl_xor(last, x, 64));
-  }
+// One block per sequence: the round's final draw and its tokens.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(SampleArgs a) {
+  __shared__ DrawShared sh;
+  const int b = blockIdx.x, C = a.n_chunks;
+  const Layout L = layout(a, kSpecPass);
+  const Decision d = L.dec[b];
+  const int n = d.n;
+  const int tr = a.gamma + n, dr = n < a.gamma ? n : tr;
+  const bool bonus = n == a.gamma;
+  const double u = philox_uniform(a.seed, a.offset, b, n, 1);
+  const double* wsum = L.wsum + (size_t)b * C;
+  const double* psum = L.psum + (size_t)b * C;
+  ChunkPick pk = pick_chunk(C, u, [&](int c) { return wsum[c]; });
+  const bool use_p = bonus || !(pk.total > 0.0);  // a residual without mass (rounding only): draw from p
+  if (!bonus && use_p) pk = pick_chunk(C, u, [&](int c) { return psum[c]; });
+  const int lo = pk.chunk * kChunk, hi = min(a.V, lo + kChunk);
+  DrawWeights wf{d.mt, d.md, d.izt, d.izd, (float)(kLog2e / (double)a.temperature), use_p ? 1 : 0};
+  const int token = draw_in_chunk(row_ptr(a, b, tr), use_p ? nullptr : row_ptr(a, b, dr), lo, hi,
+                                  pk.before, pk.target, pk.fallback, wf, sh);
+  const int lane = threadIdx.x;
   if (lane <= a.gamma) {
-    const int token = first != 0x7fffffff ? first : last;
     a.out_tokens[(size_t)b * (a.gamma + 1) + lane] =
         lane < n ? a.draft_tokens[(size_t)b * a.gamma + lane] : (lane == n ? token : -1);
     if (lane == 0) a.num_accepted[b] = n;
   }
+}
+
+// ---------------------------------------------------------------------------
+// The drafter's own draws: x[b][r] = ICDF(softmax(row / T), U(b, first_slot + r, 2)).
+// One block per (sequence, row), after the statistics pass. The weights are
+// 2^((x - M) log2(e) / T), unnormalised (the inverse CDF is scale-free).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void draw_kernel(SampleArgs a) {
+  __shared__ DrawShared sh;
+  const int r = blockIdx.x % a.rows, b = blockIdx.x / a.rows;
+  const int C = a.n_chunks;
+  const Layout L = layout(a, kDrawPass);
+  const size_t base = ((size_t)b * a.rows + r) * C;
+  const float* cmax = L.cmax + base;
+  const double* csum = L.csum + base;
+  const double cl = kLog2e / (double)a.temperature;
+  float M;
+  double Z;
+  fold_row(cmax, csum, C, cl, M, Z);
+  const double u = philox_uniform(a.seed, a.offset, b, (uint64_t)(a.first_slot + r), 2);
+  const ChunkPick pk = pick_chunk(C, u, [&](int c) {
+    const double s = csum[c];
+    return s > 0.0 ? s * exp2(((double)cmax[c] - (double)M) * cl) : 0.0;
+  });
+  const int lo = pk.chunk * kChunk, hi = min(a.V, lo + kChunk);
+  DrawWeights wf{M, 0.f, 1.0, 0.0, (float)cl, 1};
+  const int token = draw_in_chunk(row_ptr(a, b, r), nullptr, lo, hi, pk.before, pk.target, pk.fallback,
+                                  wf, sh);
+  if (threadIdx.x == 0) a.out_tokens[(size_t)b * a.rows + r] = token;
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance rate: per (sequence, draft position, chunk) the fp64 sum of
+// min(p, q) over the chunk, then an ordered fold over the chunks.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void alpha_kernel(SampleArgs a) {
+  __shared__ float sM[2];
+  __shared__ double sZ[2];
+  __shared__ double red[kWaves];
+  const int C = a.n_chunks;
+  const int c = blockIdx.x % C;
+  const int bi = blockIdx.x / C;
+  const int i = bi % a.gamma, b = bi / a.gamma;
+  const int wave = threadIdx.x >> 6;
+  const Layout L = layout(a, kAlphaPass);
+  const double cl = kLog2e / (double)a.temperature;
+  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
+  const int rq = i, rp = a.gamma + i;  // draft row i, target row i
+  float xq[kPerThread], xp[kPerThread];
+  load_strided(row_ptr(a, b, rq), lo, hi, xq);
+  load_strided(row_ptr(a, b, rp), lo, hi, xp);
+  if (wave < 2) {
+    const size_t base = ((size_t)b * a.rows + (wave == 0 ? rq : rp)) * C;
+    float M;
+    double Z;
+    fold_row(L.cmax + base, L.csum + base, C, cl, M, Z);
+    if ((threadIdx.x & 63) == 0) {
+      sM[wave] = M;
+      sZ[wave] = Z;
+    }
+  }
+  __syncthreads();
+  const float mq = sM[0], mp = sM[1];
+  const double izq = 1.0 / sZ[0], izp = 1.0 / sZ[1];
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const double q = (double)__builtin_amdgcn_exp2f((xq[e] - mq) * (float)cl) * izq;
+    const double p = (double)__builtin_amdgcn_exp2f((xp[e] - mp) * (float)cl) * izp;
+    s += p < q ? p : q;
+  }
+  s = block_sum_to_thread0(s, red);
+  if (threadIdx.x == 0) L.apart[((size_t)b * a.gamma + i) * C + c] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void alpha_fold_kernel(SampleArgs a) {
+  const int bi = blockIdx.x * kThreads + threadIdx.x;
+  if (bi >= a.B * a.gamma) return;
+  const Layout L = layout(a, kAlphaPass);
+  const double* part = L.apart + (size_t)bi * a.n_chunks;
+  double s = 0.0;
+  for (int c = 0; c < a.n_chunks; ++c) s += part[c];
+  a.alpha[bi] = s;
+}
+
+hipError_t launch_stats(const SampleArgs& a, int pass, hipStream_t stream) {
+  const size_t blocks = (size_t)a.B * a.rows * a.n_chunks;
+  hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, pass);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -490,24 +651,53 @@ __global__ __launch_bounds__(kFinalizeLanes) void finalize_kernel(SampleArgs a) 
 int32_t sample_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
 
 size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab) {
-  const size_t C = (size_t)sample_chunks(vocab), R = 2 * (size_t)gamma + 1;
-  return sizeof(double) * B * R * C + 2 * sizeof(double) * B * C +
-         2 * sizeof(double) * B * C * kThreads + sizeof(double) * B * R +
-         sizeof(float) * B * R * C + sizeof(float) * B * R + sizeof(int) * B;
+  return layout_of(nullptr, kSpecPass, B, 2 * (size_t)gamma + 1, sample_chunks(vocab), gamma, nullptr);
 }
 
-hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
-  const int R = 2 * a.gamma + 1;
-  hipLaunchKernelGGL(stats_kernel, dim3(a.n_chunks, R, a.B), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decide_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(residual_kernel, dim3(a.n_chunks, a.B), dim3(kThreads), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(kFinalizeLanes), 0, stream, a);
+size_t draft_sample_workspace_bytes(int32_t B, int32_t rows, int32_t vocab) {
+  return layout_of(nullptr, kDrawPass, B, rows, sample_chunks(vocab), 0, nullptr);
+}
+
+size_t acceptance_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab) {
+  return layout_of(nullptr, kAlphaPass, B, 2 * (size_t)gamma, sample_chunks(vocab), gamma, nullptr);
+}
+
+size_t sample_blocks(int32_t B, int32_t rows, int32_t vocab) {
+  return (size_t)B * rows * sample_chunks(vocab);
+}
+
+hipError_t launch_sample(const SampleArgs& in, hipStream_t stream) {
+  SampleArgs a = in;
+  a.rows = 2 * a.gamma + 1;
+  a.draft_rows = a.gamma;
+  if (hipError_t e = launch_stats(a, kSpecPass, stream)) return e;
+  hipLaunchKernelGGL(residual_kernel, dim3((unsigned)((size_t)a.B * a.n_chunks)), dim3(kThreads), 0, stream, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_sample(const SampleArgs& in, hipStream_t stream) {
+  SampleArgs a = in;
+  a.draft_rows = a.rows;
+  a.target_logits = nullptr;
+  a.draft_tokens = nullptr;
+  if (hipError_t e = launch_stats(a, kDrawPass, stream)) return e;
+  hipLaunchKernelGGL(draw_kernel, dim3((unsigned)((size_t)a.B * a.rows)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_acceptance(const SampleArgs& in, hipStream_t stream) {
+  SampleArgs a = in;
+  a.rows = 2 * a.gamma;
+  a.draft_rows = a.gamma;
+  a.draft_tokens = nullptr;
+  if (hipError_t e = launch_stats(a, kAlphaPass, stream)) return e;
+  hipLaunchKernelGGL(alpha_kernel, dim3((unsigned)((size_t)a.B * a.gamma * a.n_chunks)), dim3(kThreads), 0,
+                     stream, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  hipLaunchKernelGGL(alpha_fold_kernel, dim3((unsigned)(((size_t)a.B * a.gamma + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.s3r_version() == 200
+    assert lib.s3r_version() == 300
     assert lib.s3r_status_string(3) == b"S3R_ERR_WORKSPACE_TOO_SMALL"
     assert lib.s3r_status_string(99) == b"S3R_ERR_UNKNOWN"
 
@@ -106,6 +106,31 @@ def test_invalid_call_arguments():
     sneed = lib.s3r_spec_sample_workspace(2, 4, 1024)
     assert sneed > 0 and lib.s3r_spec_sample_workspace(2, 17, 1024) == 0
     assert s(2, 4, 1024, v, v, v, 1.0, 0, 0, v, v, v, sneed - 1, None) == 3
+    ds = lib.s3r_draft_sample
+    assert ds(0, 4, 1024, v, 1.0, 0, 0, 0, v, v, big, None) == 1          # num_seqs
+    assert ds(2, 0, 1024, v, 1.0, 0, 0, 0, v, v, big, None) == 1          # n_rows
+    assert ds(2, 4, 0, v, 1.0, 0, 0, 0, v, v, big, None) == 1             # vocab
+    assert ds(2, 4, 1024, v, 1.0, 0, 0, -1, v, v, big, None) == 1         # first_slot
+    assert ds(2, 4, 1024, v, float("nan"), 0, 0, 0, v, v, big, None) == 1
+    assert ds(2, 4, 1024, None, 1.0, 0, 0, 0, v, v, big, None) == 1
+    assert ds(2, 4, 1024, v, 1.0, 0, 0, 0, None, v, big, None) == 1
+    assert ds(1 << 20, 1 << 10, 1 << 20, v, 1.0, 0, 0, 0, v, v, big, None) == 2   # grid too large
+    dsneed = lib.s3r_draft_sample_workspace(2, 4, 1024)
+    assert dsneed > 0 and lib.s3r_draft_sample_workspace(2, 0, 1024) == 0
+    assert ds(2, 4, 1024, v, 1.0, 0, 0, 0, v, v, dsneed - 1, None) == 3
+    assert ds(2, 4, 1024, v, 1.0, 0, 0, 0, v, ctypes.c_void_p(FAKE + 4), big, None) == 1  # workspace
+    ar = lib.s3r_acceptance_rate
+    assert ar(0, 4, 1024, v, v, 1.0, v, v, big, None) == 1
+    assert ar(2, 0, 1024, v, v, 1.0, v, v, big, None) == 1
+    assert ar(2, 4, 0, v, v, 1.0, v, v, big, None) == 1
+    assert ar(2, 4, 1024, v, v, -1.0, v, v, big, None) == 1
+    assert ar(2, 4, 1024, None, v, 1.0, v, v, big, None) == 1
+    assert ar(2, 4, 1024, v, None, 1.0, v, v, big, None) == 1
+    assert ar(2, 4, 1024, v, v, 1.0, None, v, big, None) == 1
+    assert ar(2, 4, 1024, v, v, 1.0, ctypes.c_void_p(FAKE + 4), v, big, None) == 1  # alpha alignment
+    arneed = lib.s3r_acceptance_rate_workspace(2, 4, 1024)
+    assert arneed > 0 and lib.s3r_acceptance_rate_workspace(2, 4, 0) == 0
+    assert ar(2, 4, 1024, v, v, 1.0, v, v, arneed - 1, None) == 3
     d = lib.s3r_sparse_draft_step
     assert d(kv, None, None, v, 64, 0.1, v, v, 0, v, v, big, None) == 1      # bounds
     assert d(kv, v, None, v, 15, 0.1, v, v, 0, v, v, big, None) == 1        # budget < P
