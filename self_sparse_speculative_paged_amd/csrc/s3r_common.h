@@ -98,6 +98,59 @@ __device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t v) {
   return op(op(r0, r1), op(r2, r3));
 }
 
+// 64-bit DPP move: both halves through the same lane permutation. Lanes the
+// row mask leaves out, or whose source lies outside the row, read 0.0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask>((uint32_t)u);
+  const uint32_t hi = dpp_u32<kCtrl, kRowMask>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave, returned wave-uniform: each row of 16 lanes is summed by
+// DPP rotations, then the four row sums (as lane 0, 16, 32, 48 hold them) are
+// added in row order. The order is fixed, so the result is reproducible.
+__device__ __forceinline__ double wave_sum_f64_uniform(double v) {
+  v += dpp_f64<kDppRowRor8>(v);
+  v += dpp_f64<kDppRowRor4>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppQuadXor1>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Maximum over the wave, returned wave-uniform.
+__device__ __forceinline__ float wave_max_f32_uniform(float v) {
+  v = fmaxf(v, dpp<kDppRowRor8>(v));
+  v = fmaxf(v, dpp<kDppRowRor4>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: a shift scan inside
+// each row of 16, then the row totals carried into the rows above.
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+  x += dpp_f64<kDppRowShr1>(x);
+  x += dpp_f64<kDppRowShr2>(x);
+  x += dpp_f64<kDppRowShr4>(x);
+  x += dpp_f64<kDppRowShr8>(x);
+  x += dpp_f64<kDppRowBcast15, 0xA>(x);
+  x += dpp_f64<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+
 // Number of set bits of a wave-wide mask below this lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

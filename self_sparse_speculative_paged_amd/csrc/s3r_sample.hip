@@ -163,22 +163,10 @@ __device__ __forceinline__ void load_contiguous(const float* row, int lo, int hi
   }
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) v += __shfl_xor(v, x, 64);
-  return v;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
-__device__ __forceinline__ double wave_inclusive_scan(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(v, d, 64);
-    if (lane >= d) v += y;
-  }
-  return v;
-}
+// Wave reductions and scans on DPP (s3r_common.h): fixed orders, so every
+// result is reproducible; the sums are fp64.
+__device__ __forceinline__ double wave_sum_f64(double v) { return wave_sum_f64_uniform(v); }
+__device__ __forceinline__ double wave_inclusive_scan(double v) { return wave_incl_scan_f64(v); }
 
 // The exclusive prefix from an inclusive one: lane l gets lane l - 1's value,
 // lane 0 gets 0. The shuffle runs on every lane: a lane that reads from a lane
@@ -188,17 +176,15 @@ __device__ __forceinline__ double wave_exclusive_from(double incl) {
   return (threadIdx.x & 63) == 0 ? 0.0 : up;
 }
 
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) v = min(v, __shfl_xor(v, x, 64));
-  return v;
-}
+// Minimum of non-negative ints, and maximum of ints >= -1, over the wave.
+__device__ __forceinline__ int wave_min_i(int v) { return (int)wave_extreme_u32<false>((uint32_t)v); }
+__device__ __forceinline__ int wave_max_i(int v) { return (int)wave_extreme_u32<true>((uint32_t)(v + 1)) - 1; }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) v = max(v, __shfl_xor(v, x, 64));
-  return v;
-}
+// 2^v for a weight of the draw, the hardware fp32 exp2 as fp64. The chunk
+// masses use the same expression for their rescale 2^((chunk max - M) ...), so
+// a chunk has mass exactly when its largest token has a nonzero weight: an
+// underflow cannot leave a chosen chunk without a token to draw.
+__device__ __forceinline__ double weight_exp2(float v) { return (double)__builtin_amdgcn_exp2f(v); }
 
 // Max M and Z = sum_c csum_c * 2^((cmax_c - M) * log2(e) / T) of one row's
 // chunk statistics, folded by one wave in a fixed order (lane l takes chunks
@@ -209,85 +195,118 @@ __device__ __forceinline__ void fold_row(const float* cmax, const double* csum, 
   const int lane = threadIdx.x & 63;
   float m = kNegInf;
   for (int c = lane; c < C; c += 64) m = fmaxf(m, cmax[c]);
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
+  m = wave_max_f32_uniform(m);
   double z = 0.0;
   for (int c = lane; c < C; c += 64) {
     const double s = csum[c];
-    if (s > 0.0) z += s * exp2(((double)cmax[c] - (double)m) * cl);
+    if (s > 0.0) z += s * weight_exp2((cmax[c] - m) * (float)cl);
   }
   M = m;
   Z = wave_sum_f64(z);
 }
 
 // ---------------------------------------------------------------------------
-// Statistics pass: one block per (sequence, row, chunk).
+// Statistics pass over the (sequence, row, chunk) items, grid-stride: each
+// block reduces one item while the next one's tokens are already in flight
+// (no item's addresses depend on a load, so the prefetch is never waiting).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void stats_kernel(SampleArgs a, int pass) {
-  __shared__ float wm[kWaves];
-  __shared__ double ws[kWaves];
+struct StatsItem {
+  const float* row;
+  int b, r, c, lo, hi, tok;
+};
+
+__device__ __forceinline__ StatsItem stats_item(const SampleArgs& a, int pass, int item) {
+  StatsItem it;
   const int C = a.n_chunks;
-  const int c = blockIdx.x % C;
-  const int br = blockIdx.x / C;
-  const int r = br % a.rows, b = br / a.rows;
+  it.c = item % C;
+  const int br = item / C;
+  it.r = br % a.rows;
+  it.b = br / a.rows;
+  it.row = row_ptr(a, it.b, it.r);
+  it.lo = it.c * kChunk;
+  it.hi = min(a.V, it.lo + kChunk);
+  // the drafted token whose logit this row's accept test reads (spec_sample)
+  it.tok = -1;
+  if (pass == kSpecPass && it.r < 2 * a.gamma)
+    it.tok = a.draft_tokens[(size_t)it.b * a.gamma + (it.r < a.gamma ? it.r : it.r - a.gamma)];
+  return it;
+}
+
+__global__ __launch_bounds__(kThreads) void stats_kernel(SampleArgs a, int pass, int n_items) {
+  __shared__ float wm[2][kWaves];
+  __shared__ double ws[2][kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
-  // The drafted token whose logit this row's accept test reads (spec_sample).
-  int tok = -1;
-  if (pass == kSpecPass && r < 2 * a.gamma) tok = a.draft_tokens[(size_t)b * a.gamma + (r < a.gamma ? r : r - a.gamma)];
-  float x[kPerThread];
-  load_strided(row_ptr(a, b, r), lo, hi, x);
-  const Layout L = layout(a, pass);
-  if (tok >= lo && tok < hi) {
-    const int rel = tok - lo;
-    if ((int)threadIdx.x == ((rel >> 2) & (kThreads - 1))) {
-      const int j = 4 * (rel / (4 * kThreads)) + (rel & 3);
-      float v = x[0];
-#pragma unroll
-      for (int e = 1; e < kPerThread; ++e) v = e == j ? x[e] : v;
-      L.probe[(size_t)b * a.rows + r] = v;
-    }
-  }
-  // Wave max, then every term against it (one rounding each), summed in fp32
-  // per thread and fp64 across the wave; the four wave partials are merged by
-  // thread 0 in wave order.
-  float m = x[0];
-#pragma unroll
-  for (int e = 1; e < kPerThread; ++e) m = fmaxf(m, x[e]);
-  m = wave_xor_max<1, 32>(m);
   const float cl = (float)kLog2e / a.temperature;
-  float s = 0.f;
-  if (m != kNegInf) {
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * cl);
-  }
-  const double sd = wave_sum_f64((double)s);
-  if (lane == 0) {
-    wm[wave] = m;
-    ws[wave] = sd;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = wm[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
-    double S = 0.0;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (wm[w] != kNegInf) S += ws[w] * (double)__builtin_amdgcn_exp2f((wm[w] - M) * cl);
+  const Layout L = layout(a, pass);
+  int item = blockIdx.x;
+  if (item >= n_items) return;
+  StatsItem it = stats_item(a, pass, item);
+  float x[kPerThread];
+  load_strided(it.row, it.lo, it.hi, x);
+  for (int parity = 0;; parity ^= 1) {
+    const int next = item + gridDim.x;
+    StatsItem nt;
+    float y[kPerThread];
+    if (next < n_items) {  // uniform
+      nt = stats_item(a, pass, next);
+      load_strided(nt.row, nt.lo, nt.hi, y);
     }
-    const size_t idx = ((size_t)b * a.rows + r) * C + c;
-    L.cmax[idx] = M;
-    L.csum[idx] = S;
+    if (it.tok >= it.lo && it.tok < it.hi) {
+      const int rel = it.tok - it.lo;
+      if ((int)threadIdx.x == ((rel >> 2) & (kThreads - 1))) {
+        const int j = 4 * (rel / (4 * kThreads)) + (rel & 3);
+        float v = x[0];
+#pragma unroll
+        for (int e = 1; e < kPerThread; ++e) v = e == j ? x[e] : v;
+        L.probe[(size_t)it.b * a.rows + it.r] = v;
+      }
+    }
+    // Wave max, then every term against it (one rounding each), summed in
+    // fp32 per thread and fp64 across the wave; thread 0 merges the four wave
+    // partials in wave order. The LDS slots alternate between items, so one
+    // barrier per item suffices.
+    float m = x[0];
+#pragma unroll
+    for (int e = 1; e < kPerThread; ++e) m = fmaxf(m, x[e]);
+    m = wave_max_f32_uniform(m);
+    float sm = 0.f;
+    if (m != kNegInf) {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) sm += __builtin_amdgcn_exp2f((x[e] - m) * cl);
+    }
+    const double sd = wave_sum_f64((double)sm);
+    if (lane == 0) {
+      wm[parity][wave] = m;
+      ws[parity][wave] = sd;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float M = wm[parity][0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[parity][w]);
+      double S = 0.0;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (wm[parity][w] != kNegInf) S += ws[parity][w] * weight_exp2((wm[parity][w] - M) * cl);
+      }
+      const size_t idx = ((size_t)it.b * a.rows + it.r) * a.n_chunks + it.c;
+      L.cmax[idx] = M;
+      L.csum[idx] = S;
+    }
+    if (next >= n_items) break;
+    item = next;
+    it = nt;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) x[e] = y[e];
   }
 }
 
 // ---------------------------------------------------------------------------
 // The accept scan, in every block of a sequence: fold the round's 2 gamma + 1
-// row statistics (wave w folds rows w, w + 4, ...), then test the gamma drafts
-// in parallel (lane i of each wave tests draft i, so every wave reaches the
-// decision without another barrier).
+// row statistics (wave w folds rows w, w + 4, ...; lane l takes chunks l,
+// l + 64, ...), then test the gamma drafts in parallel (lane i of each wave
+// tests draft i, so every wave reaches the decision without another barrier).
 // ---------------------------------------------------------------------------
 struct RoundRows {
   float M[2 * 16 + 1];
@@ -295,40 +314,59 @@ struct RoundRows {
 };
 
 __device__ int round_decision(const SampleArgs& a, const Layout& L, int b, RoundRows& rr) {
+  constexpr int kRowsPerWave = (2 * 16 + 1 + kWaves - 1) / kWaves;
   const int R = 2 * a.gamma + 1, C = a.n_chunks;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const double cl = kLog2e / (double)a.temperature;
-  for (int r = wave; r < R; r += kWaves) {
-    float M;
-    double Z;
-    const size_t base = ((size_t)b * R + r) * C;
-    fold_row(L.cmax + base, L.csum + base, C, cl, M, Z);
-    if (lane == 0) {
-      rr.M[r] = M;
-      rr.Z[r] = Z;
+  // The drafted tokens' logits and every statistic this wave folds are loaded
+  // before any is used (one round trip), and the accept uniform is drawn
+  // meanwhile.
+  const int i = lane < a.gamma ? lane : 0;
+  const double lt = L.probe[(size_t)b * R + a.gamma + i];
+  const double ld = L.probe[(size_t)b * R + i];
+  const double u = philox_uniform(a.seed, a.offset, b, i, 0);
+  for (int c0 = 0; c0 < C; c0 += 64) {
+    float cm[kRowsPerWave];
+    double cs[kRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = wave + kWaves * k, c = c0 + lane;
+      const bool ok = r < R && c < C;
+      const size_t idx = ((size_t)b * R + (ok ? r : 0)) * C + (ok ? c : 0);
+      cm[k] = ok ? L.cmax[idx] : kNegInf;
+      cs[k] = ok ? L.csum[idx] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = wave + kWaves * k;
+      if (r >= R) break;  // uniform
+      const float M = wave_max_f32_uniform(cm[k]);
+      const double Z = wave_sum_f64(cs[k] > 0.0 ? cs[k] * weight_exp2((cm[k] - M) * (float)cl) : 0.0);
+      if (lane == 0) {
+        if (c0 == 0) {
+          rr.M[r] = M;
+          rr.Z[r] = Z;
+        } else {  // more than 64 chunks: fold this pass into the running values
+          // A side without mass adds nothing; rescaling it would form
+          // 0 * 2^(-inf - -inf) = NaN when every token so far is masked.
+          const float Mn = fmaxf(rr.M[r], M);
+          const double zr = rr.Z[r] > 0.0 ? rr.Z[r] * weight_exp2((rr.M[r] - Mn) * (float)cl) : 0.0;
+          const double zp = Z > 0.0 ? Z * weight_exp2((M - Mn) * (float)cl) : 0.0;
+          rr.Z[r] = zr + zp;
+          rr.M[r] = Mn;
+        }
+      }
     }
   }
   __syncthreads();
   bool reject = false;
   if (lane < a.gamma) {
-    const int i = lane;
-    const double lt = L.probe[(size_t)b * R + a.gamma + i];
-    const double ld = L.probe[(size_t)b * R + i];
     const double p = exp2((lt - (double)rr.M[a.gamma + i]) * cl) / rr.Z[a.gamma + i];
     const double q = exp2((ld - (double)rr.M[i]) * cl) / rr.Z[i];
-    const double u = philox_uniform(a.seed, a.offset, b, i, 0);
     reject = !(q > 0.0 ? (u < p / q) : (p > 0.0));
   }
   const uint64_t rej = __ballot(reject);
   return rej ? (int)__builtin_ctzll(rej) : a.gamma;
-}
-
-// 2^v for a draw weight: the hardware fp32 exp2, or the fp64 exp2 where that
-// underflows, so a finite logit never gets a zero weight while its chunk's
-// statistics (folded in fp64) give the chunk mass.
-__device__ __forceinline__ double weight_exp2(float v) {
-  const float e = __builtin_amdgcn_exp2f(v);
-  return (e != 0.f || v == kNegInf) ? (double)e : exp2((double)v);
 }
 
 // Per-thread weights of the final draw from the two rows' logits.
@@ -389,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(SampleArgs a) {
     if (threadIdx.x == 0) {
       const size_t idx = ((size_t)b * R + tr) * C + c;
       const double s = L.csum[idx];
-      const double mass = s > 0.0 ? s * exp2(((double)L.cmax[idx] - (double)rr.M[tr]) * cl) * izt : 0.0;
+      const double mass = s > 0.0 ? s * weight_exp2((L.cmax[idx] - rr.M[tr]) * (float)cl) * izt : 0.0;
       L.wsum[(size_t)b * C + c] = mass;
       L.psum[(size_t)b * C + c] = mass;
     }
@@ -441,7 +479,7 @@ __device__ ChunkPick pick_chunk(int C, double u, const Mass& mass) {
   const double incl = wave_inclusive_scan(own);
   const double excl = wave_exclusive_from(incl);
   ChunkPick pk;
-  pk.total = __shfl(incl, 63, 64);
+  pk.total = readlane_f64(incl, 63);
   pk.target = u * pk.total;
   int chunk = INT_MAX;
   double before = 0.0, run = excl;
@@ -458,7 +496,7 @@ __device__ ChunkPick pick_chunk(int C, double u, const Mass& mass) {
   pk.fallback = best == INT_MAX;
   if (pk.fallback) best = max(wave_max_i(last_pos), 0);
   const uint64_t owner = __ballot(chunk == best);
-  const double owner_before = __shfl(before, owner ? (int)__builtin_ctzll(owner) : 0, 64);
+  const double owner_before = readlane_f64(before, owner ? (int)__builtin_ctzll(owner) : 0);
   pk.before = pk.fallback ? 0.0 : owner_before;
   pk.chunk = best;
   return pk;
@@ -577,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(SampleArgs a) {
   const double u = philox_uniform(a.seed, a.offset, b, (uint64_t)(a.first_slot + r), 2);
   const ChunkPick pk = pick_chunk(C, u, [&](int c) {
     const double s = csum[c];
-    return s > 0.0 ? s * exp2(((double)cmax[c] - (double)M) * cl) : 0.0;
+    return s > 0.0 ? s * weight_exp2((cmax[c] - M) * (float)cl) : 0.0;
   });
   const int lo = pk.chunk * kChunk, hi = min(a.V, lo + kChunk);
   DrawWeights wf{M, 0.f, 1.0, 0.0, (float)cl, 1};
@@ -640,9 +678,13 @@ __global__ __launch_bounds__(kThreads) void alpha_fold_kernel(SampleArgs a) {
   a.alpha[bi] = s;
 }
 
+// Resident blocks of the statistics pass: 8 per CU (its occupancy), 256 CUs.
+constexpr int kStatsGrid = 8 * 256;
+
 hipError_t launch_stats(const SampleArgs& a, int pass, hipStream_t stream) {
-  const size_t blocks = (size_t)a.B * a.rows * a.n_chunks;
-  hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, pass);
+  const size_t items = (size_t)a.B * a.rows * a.n_chunks;
+  const unsigned grid = (unsigned)(items < (size_t)kStatsGrid ? items : (size_t)kStatsGrid);
+  hipLaunchKernelGGL(stats_kernel, dim3(grid), dim3(kThreads), 0, stream, a, pass, (int)items);
   return hipGetLastError();
 }
 
