@@ -15,7 +15,9 @@
  *   comment says "host". The caller owns every buffer and keeps it alive until
  *   the work queued on `stream` has completed. The library allocates and frees
  *   no device memory; scratch is the caller's `workspace`, sized by the
- *   matching *_workspace() query (host-only, no HIP call).
+ *   matching *_workspace() query (host-only, no HIP call). The one exception,
+ *   s3r_spec_sample_noalloc, uses a scratch array the library keeps in device
+ *   memory instead (see there).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
  *   only enqueue work: no call synchronises the device or the host (except
  *   under S3R_DEBUG).
@@ -24,7 +26,8 @@
  *   (page ids, seq_lens, token ids) is trusted unless S3R_DEBUG is set (see
  *   "Device data checks" below). No C++ exception crosses the
  *   ABI. The library keeps no state between calls; calls on different streams
- *   are safe if their outputs and workspaces are disjoint.
+ *   are safe if their outputs and workspaces are disjoint (calls of
+ *   s3r_spec_sample_noalloc on one GPU share that GPU's scratch).
  * - k_pool, v_pool, bounds, q, attention outputs, new K/V rows and every
  *   workspace must be 16-byte aligned (torch allocations are): the kernels
  *   move them as 16-byte vectors. A misaligned one is INVALID_ARGUMENT.
@@ -294,6 +297,29 @@ s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
                            const int32_t* draft_tokens, float temperature, uint64_t seed,
                            uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * s3r_spec_sample_noalloc: s3r_spec_sample for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same results from the same kernels, with the
+ * workspace taken from a scratch array the library holds in device memory
+ * (one per GPU it runs on, kept until the process ends) instead of a caller
+ * buffer. The call allocates nothing. Arguments and errors as
+ * s3r_spec_sample, except WORKSPACE_TOO_SMALL when
+ * s3r_spec_sample_workspace(num_seqs, gamma, vocab) exceeds
+ * s3r_spec_sample_noalloc_max_workspace() (4 MiB: for example B = 256,
+ * gamma = 16 at a 152K vocabulary), and HIP if the scratch's device address
+ * cannot be looked up. Every value the call reads from the scratch it first
+ * writes itself, so nothing is cleared between calls. All calls on one GPU
+ * share its scratch: two calls that may overlap on that GPU (other streams,
+ * other host threads) race and give undefined tokens; serialise them.
+ */
+size_t s3r_spec_sample_noalloc_max_workspace(void);
+s3r_status s3r_spec_sample_noalloc(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                                   const float* draft_logits, const float* target_logits,
+                                   const int32_t* draft_tokens, float temperature, uint64_t seed,
+                                   uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
+                                   void* stream);
 
 /*
  * s3r_draft_sample: the drafter's own draws, sampling directly from the

@@ -28,7 +28,7 @@ __all__ = [
     "dense_verify_attn", "spec_sample", "page_select_workspace", "attn_workspace",
     "spec_sample_workspace", "version", "sparse_draft_step", "sparse_draft_step_workspace",
     "sparse_draft_round", "kv_commit", "draft_sample", "draft_sample_workspace",
-    "acceptance_rate", "acceptance_rate_workspace",
+    "acceptance_rate", "acceptance_rate_workspace", "spec_sample_noalloc",
 ]
 
 _KV_DTYPES = {torch.float32: _lib.S3R_F32, torch.bfloat16: _lib.S3R_BF16}
@@ -379,3 +379,21 @@ def acceptance_rate(draft_logits, target_logits, temperature, alpha=None, worksp
         _dev(alpha, "alpha", torch.float64, (B, gamma)), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
         _stream(stream)), "s3r_acceptance_rate")
     return alpha
+
+
+@_on_device
+def spec_sample_noalloc(draft_logits, target_logits, draft_tokens, temperature, seed, offset,
+                        out_tokens, num_accepted, stream=None):
+    """spec_sample with the library's own device scratch: nothing is allocated,
+    so the caller passes the outputs. Calls that may overlap on one GPU share
+    that scratch and must be serialised."""
+    lib = _lib.load()
+    B, gamma, V = draft_logits.shape
+    _check(lib.s3r_spec_sample_noalloc(
+        B, gamma, V, _dev(draft_logits, "draft_logits", torch.float32),
+        _dev(target_logits, "target_logits", torch.float32, (B, gamma + 1, V)),
+        _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma)), float(temperature),
+        int(seed), int(offset), _dev(out_tokens, "out_tokens", torch.int32, (B, gamma + 1)),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)), _stream(stream)),
+        "s3r_spec_sample_noalloc")
+    return out_tokens, num_accepted

@@ -23,7 +23,8 @@ EXPORTS = [
     "s3r_dense_verify_attn", "s3r_spec_sample", "s3r_status_string", "s3r_version",
     "s3r_sparse_draft_step_workspace", "s3r_sparse_draft_step", "s3r_sparse_draft_round",
     "s3r_kv_commit", "s3r_draft_sample_workspace", "s3r_draft_sample",
-    "s3r_acceptance_rate_workspace", "s3r_acceptance_rate",
+    "s3r_acceptance_rate_workspace", "s3r_acceptance_rate", "s3r_spec_sample_noalloc_max_workspace",
+    "s3r_spec_sample_noalloc",
 ]
 
 
@@ -79,6 +80,8 @@ def load():
         "s3r_draft_sample": (i32, [i32, i32, i32, vp, f32, u64, u64, i64, vp, vp, sz, vp]),
         "s3r_acceptance_rate_workspace": (sz, [i32, i32, i32]),
         "s3r_acceptance_rate": (i32, [i32, i32, i32, vp, vp, f32, vp, vp, sz, vp]),
+        "s3r_spec_sample_noalloc_max_workspace": (sz, []),
+        "s3r_spec_sample_noalloc": (i32, [i32, i32, i32, vp, vp, vp, f32, u64, u64, vp, vp, vp]),
         "s3r_status_string": (ctypes.c_char_p, [i32]),
         "s3r_version": (i32, []),
     }

@@ -490,19 +490,26 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t 
                        workspace_bytes, stream, "s3r_dense_verify_attn");
 }
 
-s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
-                           const float* draft_logits, const float* target_logits,
-                           const int32_t* draft_tokens, float temperature, uint64_t seed,
-                           uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+s3r_status check_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab, const float* draft_logits,
+                             const float* target_logits, const int32_t* draft_tokens, float temperature,
+                             int32_t* out_tokens, int32_t* num_accepted) {
   if (num_seqs < 1 || vocab < 1 || gamma < 1 || gamma > kMaxGamma) return S3R_ERR_INVALID_ARGUMENT;
   if (!(temperature > 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARGUMENT;
   if (draft_logits == nullptr || target_logits == nullptr || draft_tokens == nullptr ||
       out_tokens == nullptr || num_accepted == nullptr)
     return S3R_ERR_INVALID_ARGUMENT;
   if (s3r::sample_blocks(num_seqs, 2 * gamma + 1, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
-  const size_t need = s3r::sample_workspace_bytes(num_seqs, gamma, vocab);
-  if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  return S3R_OK;
+}
+
+s3r_status run_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab, const float* draft_logits,
+                           const float* target_logits, const int32_t* draft_tokens, float temperature,
+                           uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
+                           void* workspace, void* stream) {
   if (s3r::debug_checks_on())
     if (s3r_status s = s3r::debug_check_tokens(draft_tokens, num_seqs, gamma, vocab,
                                                 static_cast<hipStream_t>(stream), "s3r_spec_sample"))
@@ -522,6 +529,42 @@ s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
   a.seed = seed;
   a.offset = offset;
   return from_hip(s3r::launch_sample(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                           const float* draft_logits, const float* target_logits,
+                           const int32_t* draft_tokens, float temperature, uint64_t seed,
+                           uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (s3r_status s = check_spec_sample(num_seqs, gamma, vocab, draft_logits, target_logits, draft_tokens,
+                                       temperature, out_tokens, num_accepted))
+    return s;
+  const size_t need = s3r::sample_workspace_bytes(num_seqs, gamma, vocab);
+  if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  return run_spec_sample(num_seqs, gamma, vocab, draft_logits, target_logits, draft_tokens, temperature,
+                         seed, offset, out_tokens, num_accepted, workspace, stream);
+}
+
+size_t s3r_spec_sample_noalloc_max_workspace(void) { return s3r::kStaticSampleScratchBytes; }
+
+s3r_status s3r_spec_sample_noalloc(int32_t num_seqs, int32_t gamma, int32_t vocab,
+                                   const float* draft_logits, const float* target_logits,
+                                   const int32_t* draft_tokens, float temperature, uint64_t seed,
+                                   uint64_t offset, int32_t* out_tokens, int32_t* num_accepted,
+                                   void* stream) {
+  if (s3r_status s = check_spec_sample(num_seqs, gamma, vocab, draft_logits, target_logits, draft_tokens,
+                                       temperature, out_tokens, num_accepted))
+    return s;
+  if (s3r::sample_workspace_bytes(num_seqs, gamma, vocab) > s3r::kStaticSampleScratchBytes)
+    return S3R_ERR_WORKSPACE_TOO_SMALL;
+  void* scratch = nullptr;
+  if (hipError_t e = s3r::static_sample_scratch(&scratch)) return from_hip(e);
+  return run_spec_sample(num_seqs, gamma, vocab, draft_logits, target_logits, draft_tokens, temperature,
+                         seed, offset, out_tokens, num_accepted, scratch, stream);
 }
 
 size_t s3r_draft_sample_workspace(int32_t num_seqs, int32_t n_rows, int32_t vocab) {

@@ -178,6 +178,10 @@ size_t sample_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab);
 size_t draft_sample_workspace_bytes(int32_t B, int32_t rows, int32_t vocab);
 size_t acceptance_workspace_bytes(int32_t B, int32_t gamma, int32_t vocab);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+// The allocation-free sampler's scratch: a device array of this many bytes,
+// and its address on the current device.
+constexpr size_t kStaticSampleScratchBytes = (size_t)4 << 20;
+hipError_t static_sample_scratch(void** ptr);
 hipError_t launch_draft_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_acceptance(const SampleArgs& a, hipStream_t stream);
 

@@ -31,6 +31,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <atomic>
+
 #include "s3r_common.h"
 #include "s3r_internal.h"
 
@@ -688,7 +690,30 @@ hipError_t launch_stats(const SampleArgs& a, int pass, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Scratch of s3r_spec_sample_noalloc: the same workspace layout, in a
+// file-scope device array instead of a caller-provided buffer. Each device
+// holds its own copy until the process ends.
+static __device__ __align__(256) unsigned char scratch[kStaticSampleScratchBytes];
+
 }  // namespace
+
+hipError_t static_sample_scratch(void** ptr) {
+  // The array's device address, looked up once per device with that device
+  // current (every device has its own copy at its own address). In host code
+  // the array's name is only a stand-in: kernels get this address instead.
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 int32_t sample_chunks(int32_t vocab) { return (vocab + kChunk - 1) / kChunk; }
 
