@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--config", default="qwen3_8b")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="time the headline workload only (not the other workloads of the bench line)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="wall-time budget of the oracle baseline's worker-pool phase")
     p.add_argument("--sweep", action="store_true",
@@ -389,7 +391,87 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, cfg, args.cpu_seconds)
+    if not args.no_configs:
+        # every other workload, timed the same way (the headline's buffers freed first)
+        del R, wl, kv, bounds, graphs
+        torch.cuda.empty_cache()
+        result["configs"] = other_configs(args)
     print(json.dumps(result), flush=True)
+
+
+def ragged_subset(n, seed=0):
+    """The n longest sequences of the ragged long-tail draw, in their original
+    order: the batch as it drains (short rollouts finish first)."""
+    import torch
+
+    from s3r_inputs import CONFIGS, ragged_lengths
+    full = ragged_lengths(CONFIGS["ragged"]["B"], seed=seed)
+    keep = torch.argsort(full, descending=True, stable=True)[:n].sort().values
+    return [int(full[i]) for i in keep]
+
+
+def config_summary(config, args, label, **overrides):
+    """One workload's round (graph replay), its verify and draft-step launches,
+    and its committed tokens per second, as a dict for the bench line."""
+    import torch
+
+    import self_sparse_speculative_paged_amd as s3r
+
+    dev = torch.device("cuda:0")
+    R = build_round(config, dev, seed=0, **overrides)
+    for w in range(max(1, args.warmup)):
+        R.one_round(w)
+    mean_acc, committed = R.accept_stats()
+    graphs = []
+    ms = time_runner(make_runner(R.one_round, True, graphs), args.steps, args.warmup)
+    ms_once = time_runner(make_runner(R.one_round_select_once, True, graphs), args.steps, args.warmup)
+
+    def time_call(fn):
+        return 1e3 * time_runner(make_runner(lambda _off: fn(), True, graphs), max(5, args.steps), args.warmup)
+
+    R.kv.set_seq_lens(R.wl.seq_lens[0])
+    t_step = time_call(lambda: s3r.sparse_draft_step(R.kv, R.bounds, R.q_draft[0], R.budget, R.scale,
+                                                     refresh_from=R.first_pos[0], selected=R.sel,
+                                                     num_selected=R.nsel, out=R.d_out[0], workspace=R.ws_step))
+    R.kv.set_seq_lens(R.wl.seq_lens[R.gamma])
+    t_verify = time_call(lambda: s3r.dense_verify_attn(R.kv, R.wl.q_verify, R.scale, out=R.v_out,
+                                                       workspace=R.ws_v))
+    t_sample = time_call(lambda: R.sample(0))
+    parts = step_bytes(R.cfg, R.ctx)
+    total = sum(parts.values())
+    out = {
+        "workload": label, "batch": R.B, "gamma": R.gamma, "budget_tokens": R.budget,
+        "context": R.ctx[0] if len(set(R.ctx)) == 1 else {"min": min(R.ctx), "max": max(R.ctx),
+                                                           "mean": round(sum(R.ctx) / len(R.ctx))},
+        "round_ms": round(ms, 4), "value_gbs": round(total / (ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "accepted_tokens_per_s": round(committed / (ms * 1e-3), 1),
+        "mean_accepted_per_seq": round(mean_acc, 3),
+        "verify_us": round(t_verify, 2),
+        "verify_pct_hbm_peak": round(100 * parts["verify"] / (t_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "draft_step_us": round(t_step, 2),
+        "draft_step_pct_hbm_peak": round(
+            100 * (parts["draft"] + parts["select"] + parts["bounds"]) / R.gamma / (t_step * 1e-6) / 1e9
+            / HBM_PEAK_GBS, 2),
+        "spec_sample_us": round(t_sample, 2),
+        "select_once_round_ms": round(ms_once, 4),
+        "round_bytes": int(total),
+    }
+    del R, graphs
+    torch.cuda.empty_cache()
+    return out
+
+
+def other_configs(args):
+    """The bench line's other workloads: the Qwen3-1.7B-shaped layer, the
+    aggressive budget (the whole select -> draft -> verify -> sample chain per
+    round), and the ragged long tail at 128 sequences and as it drains to 64,
+    16 and 8."""
+    res = {"qwen3_1p7b": config_summary("qwen3_1p7b", args, "qwen3_1p7b_layer"),
+           "aggressive": config_summary("aggressive", args, "aggressive_layer")}
+    for n in (128, 64, 16, 8):
+        res[f"ragged_{n}"] = config_summary("ragged", args, f"ragged_long_tail_{n}", B=n, ctx=ragged_subset(n))
+    return res
 
 
 FIDELITY_BUDGETS = (256, 512, 1024, 2048, 4096)
@@ -562,15 +644,12 @@ def shrink(args):
     JSON line per active batch size."""
     import torch
 
-    from s3r_inputs import CONFIGS, ragged_lengths
+    from s3r_inputs import CONFIGS
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = CONFIGS["ragged"]
-    full = ragged_lengths(cfg["B"], seed=0)
-    for n in cfg["shrink"]:
-        keep = torch.argsort(full, descending=True, stable=True)[:n].sort().values
-        ctx = [int(full[i]) for i in keep]
+    for n in CONFIGS["ragged"]["shrink"]:
+        ctx = ragged_subset(n)
         R = build_round("ragged", dev, seed=0, B=n, ctx=ctx)
         graphs = []
         ms = time_runner(make_runner(R.one_round, True, graphs), args.steps, args.warmup)

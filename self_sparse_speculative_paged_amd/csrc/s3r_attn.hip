@@ -269,66 +269,18 @@ template <int kD, int kG, int kThreads>
 __device__ __forceinline__ void score_row_to_lds(const AttnArgs& a, int b, int h, int seq_len,
                                                  int n, bool score, const ForcedPages& fp, float* sc,
                                                  int32_t* pt_lds) {
-  constexpr int kLpp = kD / 8;
-  constexpr int kGroups = kThreads / kLpp;  // pages per block-wide step
-  constexpr int kIter = 8;                  // pages per page group per batch
-  constexpr int kBatch = kGroups * kIter;
-  const int c = threadIdx.x % kLpp, grp = threadIdx.x / kLpp;
-  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  const int rf = a.refresh_from ? min(max(a.refresh_from[b], 0) / kPage, n) : n;
-  PageScorerBf16<kD, kG> qs;
-  qs.load(static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h * kG) * kD, c);
-  // Refreshed pages (normally just the tail page) first, so their dependent
-  // K loads overlap the first batch.
-  for (int j = rf + grp; j < n; j += kGroups) {
-    const int phys = pt[j];
-    uint4 lo, hi;
-    refresh_page_bounds_bf16<kD>(static_cast<const uint16_t*>(a.k_pool),
-                                 static_cast<uint16_t*>(a.bounds_out), a.Hkv, h, phys,
-                                 min(kPage, seq_len - kPage * j), c, lo, hi);
-    if (score) {
-      const float s = qs.score(lo, hi, a.sel_scale);
-      if (c == 0) sc[j] = j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : s;
-    }
-    if (c == 1) pt_lds[j] = phys;
-  }
-  // Pages before the refresh point in batches of kIter per page group; the
-  // next batch's page ids load while this batch's bounds are scored.
-  const uint16_t* bb = static_cast<const uint16_t*>(a.bounds);
-  int ids[kIter];
-#pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    const int j = grp + kGroups * i;
-    ids[i] = j < rf ? pt[j] : -1;
-  }
-  for (int base = 0; base < rf; base += kBatch) {
-    int cur[kIter];
-    uint4 lo[kIter], hi[kIter];
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      cur[i] = ids[i];
-      if (score && cur[i] >= 0) {
-        const uint16_t* pb = bb + ((size_t)cur[i] * a.Hkv + h) * 2 * kD + 8 * c;
-        lo[i] = load_nt16<uint4>(pb);
-        hi[i] = load_nt16<uint4>(pb + kD);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int j = base + kBatch + grp + kGroups * i;
-      ids[i] = j < rf ? pt[j] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      if (cur[i] < 0) continue;  // uniform within the page group
-      const int j = base + grp + kGroups * i;
-      if (score) {
-        const float s = qs.score(lo[i], hi[i], a.sel_scale);
-        if (c == 0) sc[j] = j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : s;
-      }
-      if (c == 1) pt_lds[j] = cur[i];
-    }
-  }
+  PageRowSource src;
+  src.q0 = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h * kG) * kD;
+  src.k_pool = static_cast<const uint16_t*>(a.k_pool);
+  src.bounds = static_cast<const uint16_t*>(a.bounds);
+  src.bounds_out = static_cast<uint16_t*>(a.bounds_out);
+  src.pt = a.page_table + (size_t)b * a.max_pages;
+  src.Hkv = a.Hkv;
+  src.h = h;
+  src.seq_len = seq_len;
+  src.rf = a.refresh_from ? min(max(a.refresh_from[b], 0) / kPage, n) : n;
+  src.scale = a.sel_scale;
+  score_pages_to_lds<kD, kG, kThreads>(src, 0, n, score, fp, sc, pt_lds);
 }
 
 // Each wave of a kW-wave workgroup owns one split of the same (sequence, kv

@@ -9,6 +9,7 @@
 #pragma once
 
 #include "s3r_common.h"
+#include "s3r_internal.h"
 
 namespace s3r {
 
@@ -98,6 +99,88 @@ __device__ __forceinline__ void refresh_page_bounds_bf16(const uint16_t* k_pool,
   uint16_t* pb = bounds_out + ((size_t)phys * Hkv + h) * 2 * kD + 8 * c;
   *reinterpret_cast<uint4*>(pb) = kmin;
   *reinterpret_cast<uint4*>(pb + kD) = kmax;
+}
+
+// Where one (sequence, kv head)'s pages are scored from: its queries, pools,
+// page-table row, and the refresh point rf (pages from rf on get their bounds
+// recomputed from K first).
+struct PageRowSource {
+  const uint16_t* q0;      // the kv head's first q head row, [kG][kD] bf16 bits
+  const uint16_t* k_pool;
+  const uint16_t* bounds;
+  uint16_t* bounds_out;
+  const int32_t* pt;       // page-table row
+  int Hkv, h, seq_len, rf;
+  float scale;
+};
+
+// Scores pages [p0, p1) of one (sequence, kv head) into sc[j - p0] (LDS) and,
+// if pt_lds is given, copies their page ids to pt_lds[j - p0]; the forced
+// pages of a once-per-round selection score +inf. Pages from the refresh point
+// on first get their bounds recomputed from K and written back. score == false
+// (every page is taken) skips the bounds reads but still refreshes.
+// A page group of kD/8 lanes scores a page; the kThreads threads take batches
+// of 8 pages per group, and the next batch's page ids load while the current
+// batch's bounds are in flight, so each batch costs one round trip.
+template <int kD, int kG, int kThreads>
+__device__ __forceinline__ void score_pages_to_lds(const PageRowSource& s, int p0, int p1, bool score,
+                                                   const ForcedPages& fp, float* sc, int32_t* pt_lds) {
+  constexpr int kLpp = kD / 8;
+  constexpr int kGroups = kThreads / kLpp;  // pages per block-wide step
+  constexpr int kIter = 8;                  // pages per page group per batch
+  constexpr int kBatch = kGroups * kIter;
+  const int c = threadIdx.x % kLpp, grp = threadIdx.x / kLpp;
+  PageScorerBf16<kD, kG> qs;
+  qs.load(s.q0, c);
+  const int rf = max(s.rf, p0);
+  // Refreshed pages (normally just the tail page) first, so their dependent
+  // K loads overlap the first batch.
+  for (int j = rf + grp; j < p1; j += kGroups) {
+    const int phys = s.pt[j];
+    uint4 lo, hi;
+    refresh_page_bounds_bf16<kD>(s.k_pool, s.bounds_out, s.Hkv, s.h, phys, min(kPage, s.seq_len - kPage * j),
+                                 c, lo, hi);
+    if (score) {
+      const float v = qs.score(lo, hi, s.scale);
+      if (c == 0) sc[j - p0] = j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : v;
+    }
+    if (pt_lds && c == 1) pt_lds[j - p0] = phys;
+  }
+  const int end = min(rf, p1);
+  int ids[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int j = p0 + grp + kGroups * i;
+    ids[i] = j < end ? s.pt[j] : -1;
+  }
+  for (int base = p0; base < end; base += kBatch) {
+    int cur[kIter];
+    uint4 lo[kIter], hi[kIter];
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      cur[i] = ids[i];
+      if (score && cur[i] >= 0) {
+        const uint16_t* pb = s.bounds + ((size_t)cur[i] * s.Hkv + s.h) * 2 * kD + 8 * c;
+        lo[i] = load_nt16<uint4>(pb);
+        hi[i] = load_nt16<uint4>(pb + kD);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int j = base + kBatch + grp + kGroups * i;
+      ids[i] = j < end ? s.pt[j] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      if (cur[i] < 0) continue;  // uniform within the page group
+      const int j = base + grp + kGroups * i;
+      if (score) {
+        const float v = qs.score(lo[i], hi[i], s.scale);
+        if (c == 0) sc[j - p0] = j >= fp.f0 && j <= fp.f1 ? __builtin_huge_valf() : v;
+      }
+      if (pt_lds && c == 1) pt_lds[j - p0] = cur[i];
+    }
+  }
 }
 
 }  // namespace s3r
