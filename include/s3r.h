@@ -125,7 +125,10 @@ size_t s3r_spec_sample_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab)
  * keys of every page touched since the last call, over the page's valid
  * tokens j*P <= t < min((j+1)*P, seq_len). This keeps the per-page key bounds
  * that s3r_page_select scores against in step with the KV cache after a KV
- * append or rollback (support for the query-aware selection rule).
+ * append or rollback (support for the query-aware selection rule). S3R
+ * Abstract: drafter and verifier are one model over one cache, so the pages
+ * the sparse draft ranks are the same pages verification later reads; their
+ * bounds must describe exactly the keys they hold at each draft step.
  *   bounds     out, [num_phys_pages][Hkv][2][D] in kv dtype.
  *   first_pos  [B] int32: for sequence b, pages from first_pos[b] / P to the
  *              last page of seq_lens[b] are recomputed. NULL = every page.
@@ -179,7 +182,9 @@ s3r_status s3r_sparse_draft_attn(const s3r_paged_kv* kv, const void* q, const in
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * s3r_sparse_draft_step: one whole draft step, the fused form of
+ * s3r_sparse_draft_step: one whole draft step (S3R Abstract: the policy
+ * drafts with sparse attention over its own KV cache, reading only part of
+ * it), the fused form of
  *   s3r_page_bounds_update(refresh_from)  (when refresh_from is not NULL)
  *   s3r_page_select(q, budget_tokens)     -> selected, num_selected
  *   s3r_sparse_draft_attn(q, selected)    -> out

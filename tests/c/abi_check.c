@@ -59,6 +59,31 @@ int main(void) {
                         0, 0, (int32_t*)fake, (int32_t*)fake, fake, 1u << 20, NULL) ==
         S3R_ERR_INVALID_ARGUMENT); /* temperature 0 */
   CHECK(s3r_kv_commit(&kv, fake, fake, NULL, 1, NULL, NULL) == S3R_ERR_INVALID_ARGUMENT);
+
+  /* the drafter's draws, the acceptance rate and the allocation-free sampler */
+  CHECK(s3r_draft_sample_workspace(2, 4, 151936) > 0);
+  CHECK(s3r_draft_sample(2, 4, 1000, (const float*)fake, 1.0f, 0, 0, -1, (int32_t*)fake, fake, 1u << 20,
+                         NULL) == S3R_ERR_INVALID_ARGUMENT); /* first_slot < 0 */
+  CHECK(s3r_draft_sample(1 << 20, 1 << 10, 1 << 20, (const float*)fake, 1.0f, 0, 0, 0, (int32_t*)fake,
+                         fake, (size_t)-1, NULL) == S3R_ERR_UNSUPPORTED); /* grid past 2^31 blocks */
+  CHECK(s3r_acceptance_rate_workspace(2, 4, 151936) > 0);
+  CHECK(s3r_acceptance_rate(2, 4, 1000, (const float*)fake, (const float*)fake, 1.0f,
+                            (double*)((uintptr_t)fake + 4), fake, 1u << 20, NULL) ==
+        S3R_ERR_INVALID_ARGUMENT); /* misaligned alpha */
+  CHECK(s3r_spec_sample_noalloc_max_workspace() == ((size_t)4 << 20));
+  CHECK(s3r_spec_sample_noalloc(4096, 16, 151936, (const float*)fake, (const float*)fake,
+                                (const int32_t*)fake, 1.0f, 0, 0, (int32_t*)fake, (int32_t*)fake, NULL) ==
+        S3R_ERR_WORKSPACE_TOO_SMALL);
+
+  /* workspace queries on large shapes: sizes, not overflow */
+  kv.num_seqs = 4096;
+  kv.max_pages_per_seq = 32768;
+  kv.total_pages_hint = 1 << 30;
+  CHECK(s3r_attn_workspace(&kv, 5, 32768) > 0);
+  CHECK(s3r_sparse_draft_step_workspace(&kv, 1 << 20) > 0);
+  CHECK(s3r_page_select_workspace(&kv, 2048) == (size_t)4096 * 2 * 32768 * 4);
+  kv.total_pages_hint = 4096 * 100; /* ragged: the order is reserved too */
+  CHECK(s3r_attn_workspace(&kv, 1, 128) > 0);
   puts("ok");
   return 0;
 }
