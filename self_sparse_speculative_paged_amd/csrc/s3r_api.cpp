@@ -178,19 +178,31 @@ struct DraftStepPlan {
   size_t workspace_bytes;  // enough for every path the call may take
 };
 
+// Whether the rank-and-attend kernel can take plan a: eight waves (its top-k
+// runs on 512 threads), the page table within that top-k, and the wave regions
+// plus the list within 64 KB of LDS. Sets the list's offset.
+bool rank_and_attend_fits(const s3r_paged_kv& kv, const s3r::SplitPlan& a, int32_t k, int32_t* list_offset) {
+  const int32_t w = a.waves_per_group;
+  const size_t regions = (size_t)a.lds_region_bytes * w;
+  const size_t list = (regions + 15) & ~(size_t)15;
+  *list_offset = (int32_t)list;
+  return kv.kv_dtype == S3R_BF16 && w == 8 && kv.max_pages_per_seq <= s3r::fused_topk_keys(w) * 64 * w &&
+         list + sizeof(int32_t) * (size_t)k <= 64 * 1024;
+}
+
 DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
   DraftStepPlan p{};
   const int32_t k = budget_tokens / kv.page_size;
+  // The attention's own plan (its LDS is capped) unless eight waves are what
+  // lets the step rank inside the attention kernel.
   p.attn = s3r::plan_attention(kv, 1, k);
-  if (kv.kv_dtype == S3R_BF16 && p.attn.row_blocks == 1 && p.attn.waves_per_group < 8)
-    p.attn = wave_plan(kv, k, 8);
+  if (kv.kv_dtype == S3R_BF16 && p.attn.row_blocks == 1 && p.attn.waves_per_group < 8) {
+    const s3r::SplitPlan w8 = wave_plan(kv, k, 8);
+    int32_t unused = 0;
+    if (rank_and_attend_fits(kv, w8, k, &unused)) p.attn = w8;
+  }
   p.select_ws = s3r::select_workspace_bytes(kv.num_seqs, kv.num_kv_heads, kv.max_pages_per_seq);
-  const int32_t w = p.attn.waves_per_group;
-  const size_t regions = (size_t)p.attn.lds_region_bytes * w;
-  const size_t list_offset = (regions + 15) & ~(size_t)15;
-  p.list_offset = (int32_t)list_offset;
-  p.fused = kv.kv_dtype == S3R_BF16 && kv.max_pages_per_seq <= s3r::fused_topk_keys(w) * 64 * w &&
-            list_offset + sizeof(int32_t) * (size_t)k <= 64 * 1024;
+  p.fused = rank_and_attend_fits(kv, p.attn, k, &p.list_offset);
   p.workspace_bytes = p.fused ? p.select_ws + p.attn.workspace_bytes
                               : (p.select_ws > p.attn.workspace_bytes ? p.select_ws : p.attn.workspace_bytes);
   if (const size_t ob = s3r::order_bytes(kv)) {

@@ -399,6 +399,9 @@ FUSED_CASES = [
     # kernel long after the rest, so the step runs eight (the four-wave, 32-key
     # top-k needs a balanced batch of long tables: test_fullsize_ragged[128])
     ("bf16", 128, 2, 8, 256, (40000,) + tuple(100 + 7 * i for i in range(63))),
+    # 2048 (sequence, kv head) pairs with k = 8750: eight waves' window tables
+    # would pass 64 KB of LDS, so the draft keeps the attention's own plan
+    ("bf16", 64, 2, 8, 140000, tuple(300 + 13 * (i % 7) for i in range(256))),
 ]
 
 
