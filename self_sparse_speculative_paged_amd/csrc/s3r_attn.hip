@@ -161,10 +161,10 @@ struct Bf16Tile {
   WindowPages w;         // the window's pages
 };
 
-template <int kD, int kNB>
-__device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint16_t* kp,
-                                               const uint16_t* vp, int Hkv, int h) {
-  const WindowPages w = t.w;
+// K of one window: A operand of S^T for its two 16-token M-blocks.
+template <int kD>
+__device__ __forceinline__ void load_bf16_k(bf16x8 (&k)[2][kD / 32], const WindowPages w, const uint16_t* kp,
+                                            int Hkv, int h) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   // M-block mb, row m = l16 holds window token 8*(m/4) + 4*mb + m%4: tokens
   // 0..15 come from page A (l16 < 8), 16..31 from page B.
@@ -174,8 +174,15 @@ __device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint1
     const int slot = (8 * (l16 >> 2) + 4 * mb + (l16 & 3)) & 15;
     const uint16_t* base = kp + (((size_t)kphys * Hkv + h) * kPage + slot) * kD + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < kD / 32; ++s) t.k[mb][s] = *reinterpret_cast<const bf16x8*>(base + 32 * s);
+    for (int s = 0; s < kD / 32; ++s) k[mb][s] = *reinterpret_cast<const bf16x8*>(base + 32 * s);
   }
+}
+
+// V of one window: A operand of O^T for each 16-wide d block.
+template <int kD>
+__device__ __forceinline__ void load_bf16_v(bf16x8 (&v)[kD / 16], const WindowPages w, const uint16_t* vp,
+                                            int Hkv, int h) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   // Contraction index (k-step s, lane group g4, element e) <-> d = 32 s + 8 g4 + e,
   // the same for K and Q: one K load instruction reads 64 contiguous bytes of
   // each of 16 token rows. K loads stay cached: two instructions share a line.
@@ -184,32 +191,41 @@ __device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint1
   const int vphys = (g4 >= 2) ? w.physB : w.physA;
   const uint16_t* vbase = vp + ((size_t)vphys * Hkv + h) * kD * kPage + l16 * kPage + 8 * (g4 & 1);
 #pragma unroll
-  for (int mb = 0; mb < kD / 16; ++mb)
-    t.v[mb] = load_nt16<bf16x8>(vbase + (size_t)16 * mb * kPage);
+  for (int mb = 0; mb < kD / 16; ++mb) v[mb] = load_nt16<bf16x8>(vbase + (size_t)16 * mb * kPage);
 }
 
 template <int kD, int kNB>
-__device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
-                                                  const bf16x8 (&qb)[kNB][kD / 32],
-                                                  const int (&qpos)[kNB], int min_qpos,
-                                                  float scale_log2, float (&m_run)[kNB],
-                                                  float (&l_run)[kNB], f32x4 (&acc)[kNB][kD / 16]) {
+__device__ __forceinline__ void load_bf16_tile(Bf16Tile<kD, kNB>& t, const uint16_t* kp,
+                                               const uint16_t* vp, int Hkv, int h) {
+  load_bf16_k<kD>(t.k, t.w, kp, Hkv, h);
+  load_bf16_v<kD>(t.v, t.w, vp, Hkv, h);
+}
+
+// qsrc(nb, q) gives row block nb's query operand for every k-step; S^T is
+// formed one row block at a time, so only that block's operand is live.
+template <int kD, int kNB, class QSrc>
+__device__ __forceinline__ void compute_bf16_kv(const bf16x8 (&k)[2][kD / 32], const bf16x8 (&v)[kD / 16],
+                                                const WindowPages w, QSrc qsrc,
+                                                const int (&qpos)[kNB], int min_qpos,
+                                                float scale_log2, float (&m_run)[kNB],
+                                                float (&l_run)[kNB], f32x4 (&acc)[kNB][kD / 16]) {
   const int lane = threadIdx.x & 63, g4 = lane >> 4;
-  const WindowPages w = t.w;
   // Only windows reaching past the first query's position, or holding an
   // invalid page, need the mask.
   const bool need_mask = w.lpA < 0 || w.lpB < 0 || 16 * max(w.lpA, w.lpB) + 15 > min_qpos;
   f32x4 sacc[2][kNB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int nb = 0; nb < kNB; ++nb) {
+    bf16x8 q[kD / 32];
+    qsrc(nb, q);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
+    for (int mb = 0; mb < 2; ++mb) {
       sacc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < kD / 32; ++s)
-        sacc[mb][nb] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[mb][s], qb[nb][s], sacc[mb][nb], 0, 0, 0);
+        sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[mb][s], q[s], sacc[mb][nb], 0, 0, 0);
     }
+  }
   // This lane's tokens: window token 8*g4 + e, e = 4*mb + i.
   const int lp = (g4 >= 2) ? w.lpB : w.lpA;
   const int pos0 = 16 * lp + 8 * (g4 & 1);
@@ -239,18 +255,32 @@ __device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
     }
 #pragma unroll
     for (int mb = 0; mb < kD / 16; ++mb) {
-      acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.v[mb], phi, acc[nb][mb], 0, 0, 0);
-      acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.v[mb], plo, acc[nb][mb], 0, 0, 0);
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[mb], phi, acc[nb][mb], 0, 0, 0);
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[mb], plo, acc[nb][mb], 0, 0, 0);
     }
   }
 }
 
+template <int kD, int kNB>
+__device__ __forceinline__ void compute_bf16_tile(const Bf16Tile<kD, kNB>& t,
+                                                  const bf16x8 (&qb)[kNB][kD / 32],
+                                                  const int (&qpos)[kNB], int min_qpos,
+                                                  float scale_log2, float (&m_run)[kNB],
+                                                  float (&l_run)[kNB], f32x4 (&acc)[kNB][kD / 16]) {
+  auto qsrc = [&](int nb, bf16x8 (&q)[kD / 32]) {
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s) q[s] = qb[nb][s];
+  };
+  compute_bf16_kv<kD, kNB>(t.k, t.v, t.w, qsrc, qpos, min_qpos, scale_log2, m_run, l_run, acc);
+}
+
 // One row block (the draft, small verify groups) fits two waves per SIMD with a
-// 2-stage pipeline. Two row blocks run one wave per SIMD with three stages;
-// three and four row blocks keep two and one, since their accumulators and
+// 2-stage pipeline. Two row blocks run one wave per SIMD with three stages.
+// Three row blocks keep their queries in LDS and run the K-ahead pipeline in
+// the kernel instead; four keep one stage, since their accumulators and
 // queries take the registers. Each depth is what fits one wave per SIMD (two
 // for one row block) without spilling: at four row blocks a second stage
-// spills and runs 2.5x slower than a single one.
+// spills, with the queries in LDS too (84 bytes even with V loaded at use).
 template <int kNB>
 constexpr int bf16_stages() { return kNB == 1 ? 2 : (kNB == 2 ? 3 : (kNB == 3 ? 2 : 1)); }
 template <int kNB>
@@ -359,15 +389,10 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int mb = 0; mb < kD / 16; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (active) {
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
-    const int32_t* pt = pt_row;
-    const int32_t* sel = sel_row;
-    const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-
-    bf16x8 qb[kNB][kD / 32];
-    int qpos[kNB];
+  // This lane's query rows: B operand of S^T per row block and k-step (the
+  // row on the lane-within-16 axis, d = 32 s + 8 g4 + e), and each row's position.
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  auto load_q = [&](bf16x8 (&qb)[kNB][kD / 32], int (&qpos)[kNB]) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       const int row = 16 * nb + l16;
@@ -383,6 +408,44 @@ void attn_bf16_kernel(AttnArgs a) {
         qpos[nb] = -1;
       }
     }
+  };
+  // Three row blocks keep the queries in LDS (one copy per workgroup, read
+  // back for each window) to free registers for a deeper K pipeline.
+  constexpr bool kQInLds = kNB == 3;
+  bf16x8(*q_lds)[kD / 32][64] = nullptr;
+  if constexpr (kQInLds) {
+    __shared__ bf16x8 q_shared[kNB][kD / 32][64];
+    q_lds = q_shared;
+    if (wave == 0) {
+      bf16x8 qb[kNB][kD / 32];
+      int qpos[kNB];
+      load_q(qb, qpos);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int s = 0; s < kD / 32; ++s) q_lds[nb][s][lane] = qb[nb][s];
+    }
+    __syncthreads();
+  }
+
+  if (active) {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
+    const int32_t* pt = pt_row;
+    const int32_t* sel = sel_row;
+
+    bf16x8 qb[kQInLds ? 1 : kNB][kD / 32];
+    int qpos[kNB];
+    if constexpr (kQInLds) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int row = 16 * nb + l16;
+        qpos[nb] = row < a.rows ? seq_len - a.nq + row % a.nq : -1;
+      }
+    } else {
+      load_q(qb, qpos);
+    }
+    (void)qb;
 
     const int min_qpos = seq_len - a.nq;
     // Resolve every window's pages once: lanes look up the split's page ids in
@@ -414,6 +477,43 @@ void attn_bf16_kernel(AttnArgs a) {
       w.physB = __builtin_amdgcn_readfirstlane(e.w);
       return w;
     };
+    if constexpr (kQInLds) {
+      // K runs kDk = 2 windows ahead of the compute and V kDv = 1: 24 KB in
+      // flight per wave, in the registers a third full stage would overflow.
+      // The queries come from LDS.
+      constexpr int kDk = 2, kDv = 1;
+      constexpr int kRk = kDk + 1, kRv = kDv + 1, kUnroll = kRk * kRv / (kRk % kRv == 0 ? kRv : 1);
+      bf16x8 kt[kRk][2][kD / 32];
+      bf16x8 vt[kRv][kD / 16];
+      WindowPages wt[kRk];
+#pragma unroll
+      for (int j = 0; j < kDk; ++j) {
+        if (j < n_win) {
+          wt[j] = pages_of(j);
+          load_bf16_k<kD>(kt[j], wt[j], kp, a.Hkv, h);
+          if (j < kDv) load_bf16_v<kD>(vt[j], wt[j], vp, a.Hkv, h);
+        }
+      }
+      for (int base = 0; base < n_win; base += kUnroll) {
+#pragma unroll
+        for (int s = 0; s < kUnroll; ++s) {
+          const int i = base + s;
+          if (i >= n_win) break;
+          if (i + kDk < n_win) {
+            wt[(s + kDk) % kRk] = pages_of(i + kDk);
+            load_bf16_k<kD>(kt[(s + kDk) % kRk], wt[(s + kDk) % kRk], kp, a.Hkv, h);
+          }
+          if (i + kDv < n_win) load_bf16_v<kD>(vt[(s + kDv) % kRv], wt[(s + kDv) % kRk], vp, a.Hkv, h);
+          asm volatile("" ::: "memory");  // keep the query reads in the loop
+          auto qsrc = [&](int nb, bf16x8 (&q)[kD / 32]) {
+#pragma unroll
+            for (int c = 0; c < kD / 32; ++c) q[c] = q_lds[nb][c][lane];
+          };
+          compute_bf16_kv<kD, kNB>(kt[s % kRk], vt[s % kRv], wt[s % kRk], qsrc, qpos, min_qpos, a.scale_log2,
+                                   m_run, l_run, acc);
+        }
+      }
+    } else {
     // kStages-deep register pipeline: while window i is computed, the loads of
     // windows i+1 .. i+kStages-1 are in flight. Three stages fit the 512
     // registers of a single wave per SIMD up to two row blocks.
@@ -438,6 +538,7 @@ void attn_bf16_kernel(AttnArgs a) {
         }
         compute_bf16_tile<kD, kNB>(t[s], qb, qpos, min_qpos, a.scale_log2, m_run, l_run, acc);
       }
+    }
     }
   }
   // This wave's partial into its LDS region: o[rows][D], then ml[rows][2]
