@@ -700,3 +700,47 @@ def test_kv_commit_skips_unallocated_pages():
     torch.cuda.synchronize()
     assert np.array_equal(f64(wl.k_pool), rK) and np.array_equal(f64(wl.v_pool), rV)
     assert np.array_equal(f64(bounds), rB)
+
+
+# Small budgets over long tables (the aggressive shape's k = 16 of 4097
+# pages), tables within the budget, and every score tied (the lowest pages
+# must win), through page_select and the draft step.
+CANDIDATE_CASES = [
+    # kv, D, G, Hkv, budget, ctx, constant keys (every score ties)
+    ("bf16", 128, 4, 2, 256, (65536, 4000, 130), False),  # 4097, 251 and 9 pages, k = 16
+    ("bf16", 128, 4, 2, 1024, (40000, 16000), False),     # k = 64 of 2501 / 1001 pages
+    ("bf16", 64, 2, 1, 256, (8000,), True),               # 500 tied pages
+    ("bf16", 64, 2, 1, 256, (20000,), True),              # 1250 tied pages
+    ("f32", 64, 2, 2, 128, (9000, 3000), False),          # fp32 scores through the separate top-k
+]
+
+
+@pytest.mark.parametrize("kv,D,G,Hkv,budget,ctx,tied", CANDIDATE_CASES)
+def test_small_budget_ranking_matches_oracle(kv, D, G, Hkv, budget, ctx, tied):
+    wl = _make(_cfg(kv, D, G, Hkv, budget=budget), list(ctx), seed=23)
+    if tied:
+        wl.k_pool.fill_(0.5)
+    scale = 1.0 / np.sqrt(D)
+    k = budget // 16
+    for step in (0, 3):
+        kvc = _kv(wl, step)
+        q = wl.draft_q(step)
+        bounds = torch.empty((wl.k_pool.shape[0], Hkv, 2, D), dtype=wl.k_pool.dtype, device=DEV)
+        s3r.page_bounds_update(kvc, bounds)
+        sel, nsel = s3r.page_select(kvc, bounds, q, budget, scale)
+        bb = bounds.clone()
+        out, sel_b, n_b = s3r.sparse_draft_step(kvc, bb, q, budget, scale,
+                                                refresh_from=(wl.seq_lens[step] - 1).contiguous())
+        torch.cuda.synchronize()
+        L = i32(wl.seq_lens[step])
+        rb = oracle.page_bounds(f64(wl.k_pool), i32(wl.page_table), L)
+        rsel, rn, rsc = oracle.page_select(rb, f64(q), i32(wl.page_table), L, budget, scale)
+        for s_, n_ in ((sel, nsel), (sel_b, n_b)):
+            if tied:  # exact: equal scores keep the lowest pages
+                assert np.array_equal(i32(s_), rsel) and np.array_equal(i32(n_), rn)
+            else:
+                check_pages(i32(s_), i32(n_), rsel, rn, rsc, k)
+        assert torch.equal(sel, sel_b)
+        ref = oracle.sparse_draft_attn(f64(q), f64(wl.k_pool), f64(wl.v_pool), i32(wl.page_table), L,
+                                       i32(sel_b), scale)
+        _check_attn(out, ref, kv)
