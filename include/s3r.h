@@ -294,7 +294,8 @@ s3r_status s3r_dense_verify_attn(const s3r_paged_kv* kv, const void* q, int32_t 
  *                 then -1.
  *   num_accepted  out [B] int32: accepted drafts n (n + 1 tokens committed).
  * Errors: INVALID_ARGUMENT for NULL pointers, num_seqs < 1, vocab < 1, gamma
- * outside 1..16, temperature not finite and > 0; WORKSPACE_TOO_SMALL.
+ * outside 1..16, temperature not finite and > 0; UNSUPPORTED when
+ * num_seqs * (2 * gamma + 1) * ceil(vocab / 4096) >= 2^31; WORKSPACE_TOO_SMALL.
  * Deterministic: no floating-point atomics; reductions run in a fixed order.
  */
 s3r_status s3r_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab,

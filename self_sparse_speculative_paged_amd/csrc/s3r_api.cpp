@@ -514,7 +514,7 @@ s3r_status check_spec_sample(int32_t num_seqs, int32_t gamma, int32_t vocab, con
   if (draft_logits == nullptr || target_logits == nullptr || draft_tokens == nullptr ||
       out_tokens == nullptr || num_accepted == nullptr)
     return S3R_ERR_INVALID_ARGUMENT;
-  if (s3r::sample_blocks(num_seqs, 2 * gamma + 1, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
+  if (s3r::sample_blocks(num_seqs, 2 * gamma + 1, vocab) >= kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   return S3R_OK;
 }
 
@@ -590,7 +590,7 @@ s3r_status s3r_draft_sample(int32_t num_seqs, int32_t n_rows, int32_t vocab, con
   if (num_seqs < 1 || n_rows < 1 || vocab < 1 || first_slot < 0) return S3R_ERR_INVALID_ARGUMENT;
   if (!(temperature > 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARGUMENT;
   if (logits == nullptr || tokens == nullptr) return S3R_ERR_INVALID_ARGUMENT;
-  if (s3r::sample_blocks(num_seqs, n_rows, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
+  if (s3r::sample_blocks(num_seqs, n_rows, vocab) >= kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::draft_sample_workspace_bytes(num_seqs, n_rows, vocab);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
   s3r::SampleArgs a{};
@@ -622,7 +622,7 @@ s3r_status s3r_acceptance_rate(int32_t num_seqs, int32_t gamma, int32_t vocab,
   if (draft_logits == nullptr || target_logits == nullptr || alpha == nullptr)
     return S3R_ERR_INVALID_ARGUMENT;
   if ((reinterpret_cast<uintptr_t>(alpha) & 7) != 0) return S3R_ERR_INVALID_ARGUMENT;
-  if (s3r::sample_blocks(num_seqs, 2 * gamma, vocab) > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
+  if (s3r::sample_blocks(num_seqs, 2 * gamma, vocab) >= kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::acceptance_workspace_bytes(num_seqs, gamma, vocab);
   if (s3r_status s = check_workspace(workspace, workspace_bytes, need)) return s;
   s3r::SampleArgs a{};

@@ -115,6 +115,11 @@ def test_invalid_call_arguments():
     assert ds(2, 4, 1024, None, 1.0, 0, 0, 0, v, v, big, None) == 1
     assert ds(2, 4, 1024, v, 1.0, 0, 0, 0, None, v, big, None) == 1
     assert ds(1 << 20, 1 << 10, 1 << 20, v, 1.0, 0, 0, 0, v, v, big, None) == 2   # grid too large
+    # exactly 2^31 blocks (32768 x 16 rows x 4096 chunks) is refused; one row fewer
+    # passes the grid check and stops at the workspace
+    assert ds(1 << 15, 16, 1 << 24, v, 1.0, 0, 0, 0, v, v, 1, None) == 2
+    assert ds(1 << 15, 15, 1 << 24, v, 1.0, 0, 0, 0, v, v, 1, None) == 3
+    assert s(1 << 15, 8, 1 << 24, v, v, v, 1.0, 0, 0, v, v, v, big, None) == 2   # 17 rows x 2^27 > 2^31
     dsneed = lib.s3r_draft_sample_workspace(2, 4, 1024)
     assert dsneed > 0 and lib.s3r_draft_sample_workspace(2, 0, 1024) == 0
     assert ds(2, 4, 1024, v, 1.0, 0, 0, 0, v, v, dsneed - 1, None) == 3
@@ -128,6 +133,7 @@ def test_invalid_call_arguments():
     assert ar(2, 4, 1024, v, None, 1.0, v, v, big, None) == 1
     assert ar(2, 4, 1024, v, v, 1.0, None, v, big, None) == 1
     assert ar(2, 4, 1024, v, v, 1.0, ctypes.c_void_p(FAKE + 4), v, big, None) == 1  # alpha alignment
+    assert ar(1 << 15, 8, 1 << 24, v, v, 1.0, v, v, big, None) == 2  # 16 rows x 2^27 chunks = 2^31 blocks
     arneed = lib.s3r_acceptance_rate_workspace(2, 4, 1024)
     assert arneed > 0 and lib.s3r_acceptance_rate_workspace(2, 4, 0) == 0
     assert ar(2, 4, 1024, v, v, 1.0, v, v, arneed - 1, None) == 3
