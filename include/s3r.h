@@ -88,7 +88,12 @@ typedef int32_t s3r_status;
 
 typedef enum { S3R_F32 = 0, S3R_BF16 = 1 } s3r_dtype;
 
-/* Host struct describing caller-owned device buffers of one paged KV cache. */
+/* Host struct describing caller-owned device buffers of one paged KV cache.
+   Every call that takes one returns INVALID_ARGUMENT for non-positive sizes,
+   Hq not a multiple of Hkv, NULL or non-16-byte-aligned pools, or NULL
+   page_table/seq_lens; UNSUPPORTED for another dtype, D or P, Hq/Hkv > 8, or
+   num_seqs * num_q_heads > 2^24 (the kernels index (sequence, head) pairs and
+   their grids in 32 bits). */
 typedef struct {
   int32_t num_seqs;          /* B */
   int32_t num_q_heads;       /* Hq */

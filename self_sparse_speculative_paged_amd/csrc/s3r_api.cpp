@@ -33,6 +33,7 @@ s3r_status check_kv(const s3r_paged_kv* kv) {
   if (kv->head_dim != 64 && kv->head_dim != 128) return S3R_ERR_UNSUPPORTED;
   if (kv->page_size != 16) return S3R_ERR_UNSUPPORTED;
   if (kv->num_q_heads / kv->num_kv_heads > 8) return S3R_ERR_UNSUPPORTED;
+  if ((int64_t)kv->num_seqs * kv->num_q_heads > ((int64_t)1 << 24)) return S3R_ERR_UNSUPPORTED;
   return S3R_OK;
 }
 

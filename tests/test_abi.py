@@ -49,6 +49,8 @@ BAD_KV = [
     (dict(v_pool=None), 1), (dict(page_table=None), 1), (dict(seq_lens=None), 1),
     (dict(head_dim=96), 2), (dict(page_size=32), 2), (dict(kv_dtype=7), 2),
     (dict(num_q_heads=18, num_kv_heads=2), 2),
+    (dict(num_seqs=(1 << 22) + 1), 2),   # num_seqs * num_q_heads past 2^24
+    (dict(num_seqs=1 << 30, num_q_heads=8, num_kv_heads=8), 2),
 ]
 
 
