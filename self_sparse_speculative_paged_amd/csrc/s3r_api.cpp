@@ -80,7 +80,7 @@ s3r_status run_attention(const s3r_paged_kv* kv, const void* q, const int32_t* s
                          size_t ws_bytes, void* stream, const char* where) {
   if (s3r_status s = check_attention(kv, q, n_q, scale, out_dtype, out)) return s;
   const int32_t max_items = sel ? ksel : kv->max_pages_per_seq;
-  const s3r::SplitPlan plan = s3r::plan_attention(*kv, n_q, max_items);
+  const s3r::SplitPlan plan = s3r::plan_attention(*kv, n_q, max_items, sel == nullptr);
   if (s3r_status s = check_workspace(ws, ws_bytes, attn_call_workspace(*kv, plan))) return s;
   if (s3r_status s = debug_kv(*kv, stream, where)) return s;
   s3r::AttnArgs a = attn_args(kv, plan, q, sel, ksel, n_q, scale, out_dtype, out, ws);
@@ -118,6 +118,7 @@ s3r::AttnArgs attn_args(const s3r_paged_kv* kv, const s3r::SplitPlan& plan, cons
   a.waves_per_group = plan.waves_per_group;
   a.n_groups = plan.n_groups;
   a.lds_region_bytes = plan.lds_region_bytes;
+  a.staged = plan.staged;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_bf16 = out_dtype == S3R_BF16;
   return a;
@@ -196,7 +197,7 @@ DraftStepPlan plan_draft_step(const s3r_paged_kv& kv, int32_t budget_tokens) {
   const int32_t k = budget_tokens / kv.page_size;
   // The attention's own plan (its LDS is capped) unless eight waves are what
   // lets the step rank inside the attention kernel.
-  p.attn = s3r::plan_attention(kv, 1, k);
+  p.attn = s3r::plan_attention(kv, 1, k, false);
   if (kv.kv_dtype == S3R_BF16 && p.attn.row_blocks == 1 && p.attn.waves_per_group < 8) {
     const s3r::SplitPlan w8 = wave_plan(kv, k, 8);
     int32_t unused = 0;
@@ -298,7 +299,10 @@ size_t s3r_page_select_workspace(const s3r_paged_kv* kv, int32_t budget_tokens) 
 
 size_t s3r_attn_workspace(const s3r_paged_kv* kv, int32_t n_queries, int32_t max_pages_attended) {
   if (check_kv(kv) != S3R_OK || n_queries < 1 || max_pages_attended < 1) return 0;
-  return attn_call_workspace(*kv, s3r::plan_attention(*kv, n_queries, max_pages_attended));
+  // enough for either kind of call: a dense verify or a sparse attention
+  const size_t dense = attn_call_workspace(*kv, s3r::plan_attention(*kv, n_queries, max_pages_attended, true));
+  const size_t sparse = attn_call_workspace(*kv, s3r::plan_attention(*kv, n_queries, max_pages_attended, false));
+  return dense > sparse ? dense : sparse;
 }
 
 size_t s3r_spec_sample_workspace(int32_t num_seqs, int32_t gamma, int32_t vocab) {

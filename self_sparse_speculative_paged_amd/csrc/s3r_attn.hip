@@ -564,6 +564,253 @@ void attn_bf16_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 KV, head dim 128, four row blocks: K/V windows staged in LDS.
+// ---------------------------------------------------------------------------
+// At 49..64 rows one wave's accumulators and queries leave room for a single
+// register stage. Here a workgroup of kNB waves streams one split of one
+// (sequence, kv head) through a ring of kR LDS slots of one window each (K
+// 8 KB, then V 8 KB), and wave nb computes row block nb of every window: a
+// wave holds one row block's state, and the bytes in flight are set by the
+// ring, not by registers. The window's sixteen 1 KB direct-to-LDS loads
+// (global_load_lds_dwordx4, each lane's 16 bytes landing at lane * 16) are
+// dealt round-robin over the waves. Streaming through these loads tops out
+// near 5.5 TB/s on gfx950 (measured with the compute taken out), below what
+// the register pipeline reaches at up to three row blocks, so only four row
+// blocks take this kernel.
+//
+// Synchronisation, per window i, in every wave:
+//   s_waitcnt vmcnt(n)  this wave's loads of window i have landed in LDS (its
+//                       later loads, windows i+1 .. i+kR-2, may still fly;
+//                       loads return in order);
+//   s_barrier           so have every wave's; and every wave has finished
+//                       reading window i-1, whose slot is refilled next;
+//   issue window i+kR-1 into slot (i-1) mod kR, then read slot i mod kR.
+// Each wave waits for its LDS reads (lgkmcnt(0)) before the barrier, and
+// compiler barriers keep every LDS read between its two hardware barriers.
+//
+// LDS layout of a slot, chosen so each 16-lane group of a ds_read_b128 hits
+// all 64 banks once:
+//   K: window token t (0..31) at row t * 256 B; logical 16-byte chunk c of the
+//      row at physical chunk c ^ (t % 16) ^ (4 * (t / 16)).
+//   V: page p (A, B) at 8192 + 4096 p; d at 32 d; token half e (0: tokens
+//      0..7, 1: 8..15) at physical half e ^ ((d / 8) % 2).
+constexpr int kStagedSlot = 16384;
+constexpr int kStagedLoads = 16;  // 1 KB loads per window
+
+template <int kCount>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(kCount >= 0 && kCount < 64, "vmcnt is 6 bits");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14;
+  // expcnt and lgkmcnt left at their maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((kCount & 15) | (7 << 4) | (15 << 8) | ((kCount >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// This wave's loads of a window before the barrier lets it be read: the
+// waves below kStagedLoads % kNB carry one load more.
+template <int kNB, int kAhead>
+__device__ __forceinline__ void wait_own_loads(int wave, bool full) {
+  constexpr int kLo = kStagedLoads / kNB, kHi = (kStagedLoads + kNB - 1) / kNB;
+  if (!full) {
+    wait_vm<0>();
+  } else if (wave < kStagedLoads % kNB) {
+    wait_vm<kAhead * kHi>();
+  } else {
+    wait_vm<kAhead * kLo>();
+  }
+}
+
+// One 8-byte LDS read that waits for itself (lgkmcnt(0)) in the same asm
+// block, and that the compiler therefore does not order against the
+// direct-to-LDS loads in flight.
+__device__ __forceinline__ uint64_t ds_read_lone(const void* p) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  uint64_t r;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+template <int kNB, int kR>
+__global__ __launch_bounds__(64 * kNB) void attn_bf16_staged_kernel(AttnArgs a) {
+  constexpr int kD = 128;
+  constexpr int kLoads = (kStagedLoads + kNB - 1) / kNB;  // per wave, at most
+  static_assert(kR >= 3 && (kR - 2) * kLoads < 64, "ring depth");
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = blockIdx.x % a.n_groups;
+  const int pair = blockIdx.x / a.n_groups;
+  const int h = pair % a.Hkv;
+  const int b = a.order ? a.order[pair / a.Hkv] : pair / a.Hkv;
+  const int seq_len = a.seq_lens[b];
+  const int n_pages = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
+  const int n_items = n_pages;
+  const int pps = split_pages(a, n_items);
+  const int j0 = group * pps;
+  if (j0 >= n_items && a.n_groups > 1) return;  // the combine skips an empty group
+  const int j1 = min(j0 + pps, n_items);
+  const int n_win = j0 < n_items ? (j1 - j0 + 1) / 2 : 0;
+
+  extern __shared__ int4 lds[];
+  char* ring = reinterpret_cast<char*>(lds);
+
+  // This wave's row block: the B operand of S^T per k-step and the row's position.
+  const int row = 16 * wave + l16;
+  bf16x8 qb[kD / 32];
+  int qpos[1] = {-1};
+  if (row < a.rows) {
+    const int gl = row / a.nq, i = row % a.nq;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+    qpos[0] = seq_len - a.nq + i;
+  } else {
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s) qb[s] = bf16x8{};
+  }
+  const int min_qpos = seq_len - a.nq;
+
+  // Source offsets (elements, within one page's (kv head) block) of this
+  // wave's loads: load j < 8 is K rows 4 (j % 4) .. +3 of page j / 4, load
+  // j >= 8 is V rows d = 32 (j % 4) .. +31 of page (j - 8) / 4, each lane's
+  // chunk chosen so it lands at its swizzled place.
+  int goff[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int j = wave + kNB * i;
+    const int page = (j & 7) >> 2;
+    if (j < 8) {
+      const int rr = 4 * (j & 3) + (lane >> 4);
+      goff[i] = rr * kD + 8 * ((lane & 15) ^ rr ^ (4 * page));
+    } else {
+      const int d = 32 * (j & 3) + (lane >> 1);
+      goff[i] = d * kPage + 8 * ((lane & 1) ^ ((d >> 3) & 1));
+    }
+  }
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
+  const size_t head_off = (size_t)h * kPage * kD;
+  const size_t page_stride = (size_t)a.Hkv * kPage * kD;
+
+  // The split's physical page pairs, one 8-byte entry per window, after the
+  // ring. They are read back as each window is issued through ds_read_lone:
+  // hipcc, unable to tell this table from the ring, makes an ordinary read of
+  // it wait for every direct-to-LDS load in flight.
+  int2* win_tab = reinterpret_cast<int2*>(ring + kR * kStagedSlot);
+  {
+    const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+    for (int wi = threadIdx.x; wi < n_win; wi += 64 * kNB) {
+      const int lp = j0 + 2 * wi;
+      win_tab[wi] = int2{pt[lp], pt[min(lp + 1, j1 - 1)]};
+    }
+  }
+  __syncthreads();
+  WindowPages wt[kR];
+  auto issue = [&](int wi, int sl) {
+    const uint64_t e = ds_read_lone(win_tab + wi);
+    const int physA = __builtin_amdgcn_readfirstlane((int)(uint32_t)e);
+    const int physB = __builtin_amdgcn_readfirstlane((int)(uint32_t)(e >> 32));
+    wt[sl].lpA = j0 + 2 * wi;
+    wt[sl].lpB = j0 + 2 * wi + 1 < j1 ? j0 + 2 * wi + 1 : -1;
+    wt[sl].physA = wt[sl].physB = 0;
+    char* dst = ring + sl * kStagedSlot;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int j = wave + kNB * i;
+      if (j < kStagedLoads) {
+        const int phys = (j & 4) ? physB : physA;
+        const uint16_t* src = (j < 8 ? kp : vp) + (size_t)phys * page_stride + head_off + goff[i];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16, 0, 0);
+      }
+    }
+  };
+
+  // This lane's LDS read offsets within a slot (see the layout above).
+  int koff[2][kD / 32];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int pB = l16 >> 3;
+    const int tok = 8 * ((l16 >> 2) & 1) + 4 * mb + (l16 & 3);
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s)
+      koff[mb][s] = (16 * pB + tok) * 256 + 16 * ((4 * s + g4) ^ tok ^ (4 * pB));
+  }
+  const int voff = 8192 + 4096 * (g4 >> 1) + 32 * l16 + 16 * ((g4 & 1) ^ ((l16 >> 3) & 1));
+
+  float m_run[1] = {kNegInf}, l_run[1] = {0.f};
+  f32x4 acc[1][kD / 16];
+#pragma unroll
+  for (int mb = 0; mb < kD / 16; ++mb) acc[0][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto qsrc = [&](int, bf16x8 (&q)[kD / 32]) {
+#pragma unroll
+    for (int s = 0; s < kD / 32; ++s) q[s] = qb[s];
+  };
+
+  wait_vm<0>();  // the queries, before any load below is counted
+#pragma unroll
+  for (int wi = 0; wi < kR - 1; ++wi)
+    if (wi < n_win) issue(wi, wi);
+  for (int base = 0; base < n_win; base += kR) {
+#pragma unroll
+    for (int s = 0; s < kR; ++s) {
+      const int wi = base + s;
+      if (wi >= n_win) break;
+      asm volatile("" ::: "memory");
+      wait_own_loads<kNB, kR - 2>(wave, wi + kR - 2 < n_win);
+      wait_lgkm0();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (wi + kR - 1 < n_win) issue(wi + kR - 1, (s + kR - 1) % kR);
+      const char* slot = ring + s * kStagedSlot;
+      bf16x8 k[2][kD / 32], v[kD / 16];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int c = 0; c < kD / 32; ++c) k[mb][c] = *reinterpret_cast<const bf16x8*>(slot + koff[mb][c]);
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb) v[mb] = *reinterpret_cast<const bf16x8*>(slot + voff + 512 * mb);
+      compute_bf16_kv<kD, 1>(k, v, wt[s], qsrc, qpos, min_qpos, a.scale_log2, m_run, l_run, acc);
+    }
+  }
+
+  // This wave's rows: the final output, or its group's partial.
+  const float l = wave_xor_sum<16, 32>(l_run[0]);
+  if (row < a.rows) {
+    if (a.n_groups == 1) {
+      const int gl = row / a.nq, i = row % a.nq;
+      const size_t ob = (((size_t)b * a.nq + i) * a.Hq + h * a.G + gl) * kD + 4 * g4;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb) {
+        const f32x4 o = acc[0][mb] * inv;
+        if (a.out_bf16) {
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + 16 * mb) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ob + 16 * mb) = o;
+        }
+      }
+    } else {
+      const size_t item = ((size_t)b * a.Hkv + h) * a.n_groups + group;
+      if (g4 == 0) {
+        a.part_ml[(item * a.rows + row) * 2 + 0] = m_run[0];
+        a.part_ml[(item * a.rows + row) * 2 + 1] = l;
+      }
+      float* o = a.part_o + (item * a.rows + row) * kD + 4 * g4;
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb) *reinterpret_cast<f32x4*>(o + 16 * mb) = acc[0][mb];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 KV: one page (16 tokens) per window on MFMA 16x16x4 f32.
 // ---------------------------------------------------------------------------
 template <int kD>
@@ -834,8 +1081,27 @@ hipError_t launch_fused_draft(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int kNB>
+hipError_t launch_staged(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.n_groups));
+  hipLaunchKernelGGL((attn_bf16_staged_kernel<kNB, kStagedRing>), grid, dim3(64 * kNB),
+                     staged_lds_bytes(a.pages_per_split), stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_groups == 1) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<128, false>), dim3((unsigned)((size_t)a.B * a.nq * a.Hq)),
+                     dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int kD, bool kSparse>
 hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
+  if constexpr (kD == 128 && !kSparse) {
+    if (a.staged) {
+      if (dt != S3R_BF16) return hipErrorInvalidValue;
+      if ((a.rows + 15) / 16 != 4) return hipErrorInvalidValue;
+      return launch_staged<4>(a, stream);
+    }
+  }
   switch ((a.rows + 15) / 16) {
     case 1: return launch_typed<kD, 1, kSparse>(a, dt, stream);
     case 2: return launch_typed<kD, 2, kSparse>(a, dt, stream);
@@ -847,7 +1113,7 @@ hipError_t launch_nb(const AttnArgs& a, s3r_dtype dt, hipStream_t stream) {
 
 }  // namespace
 
-SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items) {
+SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items, bool dense) {
   // As many splits as resident waves: 256 CUs x 4 SIMDs x (2 waves per SIMD
   // for one MFMA row block, 1 otherwise).
   // A single query (a draft step over a short selection) splits down to one
@@ -886,6 +1152,13 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
     const int wmax = p.row_blocks == 1 ? 8 : 4;
     while (w < wmax && w < p.n_splits) w *= 2;
     while (w > 1 && (size_t)w * p.lds_region_bytes > kMaxGroupLds) w /= 2;
+  }
+  // Dense bf16, head dim 128, four row blocks: one split per workgroup, K/V
+  // staged through LDS.
+  if (dense && kv.kv_dtype == S3R_BF16 && kv.head_dim == 128 && p.row_blocks == 4) {
+    p.staged = 1;
+    w = 1;
+    p.lds_region_bytes = 0;
   }
   p.waves_per_group = w;
   p.n_groups = (p.n_splits + w - 1) / w;

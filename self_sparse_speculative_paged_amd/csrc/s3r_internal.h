@@ -22,9 +22,18 @@ struct SplitPlan {
   int32_t n_groups;         // workgroups per (sequence, kv head)
   int32_t lds_region_bytes; // per-wave LDS region (window table, then partial)
   size_t workspace_bytes;   // global partials: only when n_groups > 1 (or fp32)
+  int32_t staged;           // K/V staged through an LDS ring, one split per workgroup
 };
 
-SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items);
+// The LDS-staged kernel (bf16 dense verify, head dim 128, 49..64 rows): a
+// ring of kStagedRing window slots of 16 KB, then the split's page pairs.
+constexpr int32_t kStagedRing = 4;
+inline size_t staged_lds_bytes(int32_t pages_per_split) {
+  return (size_t)kStagedRing * 16384 + 8 * (size_t)((pages_per_split + 1) / 2);
+}
+
+// dense: every page of each sequence (the verify); else a selection of max_items.
+SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_items, bool dense);
 
 // Once-per-round selection: logical pages [f0, f1] hold the positions of the
 // round's gamma draft queries, seq_len - 1 .. seq_len + gamma - 2 (seq_len at
@@ -59,6 +68,7 @@ struct AttnArgs {
   int32_t B, Hq, Hkv, G, D, max_pages, nq, ksel;
   int32_t rows, pages_per_split, n_splits;
   int32_t waves_per_group, n_groups, lds_region_bytes;
+  int32_t staged;         // SplitPlan::staged
   float scale_log2;       // softmax_scale * log2(e)
   int32_t out_bf16;
   // Fused draft step only: page scores [B][Hkv][max_pages]; the selection is

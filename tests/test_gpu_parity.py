@@ -67,6 +67,11 @@ VERIFY_CASES = [
     ("bf16", 128, 3, 2, 5, (500, 90)),           # 18 rows: two row blocks
     ("bf16", 64, 5, 2, 2, (300, 33)),            # 15 rows: one row block
     ("bf16", 128, 7, 1, 8, (260, 40)),           # 63 rows: four row blocks
+    ("bf16", 128, 4, 2, 8, (200, 9, 31)),         # 36 rows, one split per (sequence, kv head)
+    ("bf16", 128, 5, 3, 7, (3000, 1500, 17, 260)),  # 40 rows, many splits, odd page counts
+    # four row blocks at D=128: K/V staged through LDS
+    ("bf16", 128, 8, 2, 7, (200, 9, 31)),         # 64 rows, one split: output written in place
+    ("bf16", 128, 7, 3, 8, (3000, 1500, 17, 260)),  # 63 rows, many splits, odd page counts
     ("f32", 128, 6, 1, 3, (200, 17)),            # 24 rows, fp32
     # gamma = 0: one query per sequence, a plain dense decode step
     ("bf16", 128, 4, 2, 0, (1000, 77, 1)),
