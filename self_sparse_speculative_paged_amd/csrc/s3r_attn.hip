@@ -152,6 +152,97 @@ __device__ __forceinline__ void merge_group(const AttnArgs& a, int b, int h, int
 }
 
 // ---------------------------------------------------------------------------
+// Direct-to-LDS loads: waits placed by hand
+// ---------------------------------------------------------------------------
+// global_load_lds_dwordx4 writes each lane's 16 bytes at LDS address base +
+// lane * 16 and counts on vmcnt like any vector load; loads return in order.
+// hipcc does not order LDS reads of such a destination after the load, so every
+// kernel that uses them waits on vmcnt itself before reading.
+constexpr int kStagedSlot = 16384;
+constexpr int kStagedLoads = 16;  // 1 KB loads per window
+
+template <int kCount>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(kCount >= 0 && kCount < 64, "vmcnt is 6 bits");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14;
+  // expcnt and lgkmcnt left at their maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((kCount & 15) | (7 << 4) | (15 << 8) | ((kCount >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// This wave's loads of a window before the barrier lets it be read: the
+// waves below kStagedLoads % kNB carry one load more.
+template <int kNB, int kAhead>
+__device__ __forceinline__ void wait_own_loads(int wave, bool full) {
+  constexpr int kLo = kStagedLoads / kNB, kHi = (kStagedLoads + kNB - 1) / kNB;
+  if (!full) {
+    wait_vm<0>();
+  } else if (wave < kStagedLoads % kNB) {
+    wait_vm<kAhead * kHi>();
+  } else {
+    wait_vm<kAhead * kLo>();
+  }
+}
+
+// LDS reads that wait for themselves (lgkmcnt(0)) in the same asm block, and
+// that the compiler therefore does not order against the direct-to-LDS loads
+// in flight: hipcc makes an ordinary LDS read it cannot tell apart from a
+// direct-to-LDS destination wait for every such load (vmcnt(0)).
+__device__ __forceinline__ uint64_t ds_read_lone(const void* p) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  uint64_t r;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+__device__ __forceinline__ int4 ds_read_lone16(const void* p) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+  return int4{(int)r.x, (int)r.y, (int)r.z, (int)r.w};
+}
+
+// K of one window (two pages of 16 tokens at head dim 128, 8 KB) in LDS:
+// window token t at row t * 256 B, its logical 16-byte chunk c at physical
+// chunk c ^ (t % 16) ^ (4 * (t / 16)), so every 16-lane group of the operand
+// reads below hits all 64 banks once. Load j (0..7, 1 KB) fills rows
+// 4 (j % 4) .. +3 of page j / 4; this is the lane's source offset (elements,
+// within the page's kv-head block).
+__device__ __forceinline__ int k_dma_offset(int j, int lane) {
+  const int rr = 4 * (j & 3) + (lane >> 4);
+  return rr * 128 + 8 * ((lane & 15) ^ rr ^ (4 * (j >> 2)));
+}
+
+// LDS offset of the lane's K operand for M-block mb and k-step s (the token
+// order of load_bf16_k).
+__device__ __forceinline__ int k_lds_offset(int mb, int s, int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4, pB = l16 >> 3;
+  const int tok = 8 * ((l16 >> 2) & 1) + 4 * mb + (l16 & 3);
+  return (16 * pB + tok) * 256 + 16 * ((4 * s + g4) ^ tok ^ (4 * pB));
+}
+
+// The eight 1 KB direct-to-LDS loads of one window's K into dst.
+__device__ __forceinline__ void dma_k_window(char* dst, const uint16_t* kp, int physA, int physB,
+                                             size_t page_stride, size_t head_off, const int (&goff)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint16_t* src = kp + (size_t)(j < 4 ? physA : physB) * page_stride + head_off + goff[j];
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16, 0, 0);
+  }
+}
+
+// Where a wave's K ring starts in its LDS region: after its window table.
+__host__ __device__ constexpr int k_ring_offset(int pages_per_split) {
+  return (16 * ((pages_per_split + 1) / 2) + 255) & ~255;
+}
+constexpr int kKRingSlots = 3;
+constexpr int kKRingBytes = kKRingSlots * 8192;
+
+// ---------------------------------------------------------------------------
 // bf16 KV
 // ---------------------------------------------------------------------------
 template <int kD, int kNB>
@@ -411,7 +502,11 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   // Three row blocks keep the queries in LDS (one copy per workgroup, read
   // back for each window) to free registers for a deeper K pipeline.
-  constexpr bool kQInLds = kNB == 3;
+  // A dense verify at head dim 128 instead keeps K in an LDS ring and the
+  // queries in registers (an ordinary LDS read of them would wait for every
+  // direct-to-LDS load in flight).
+  constexpr bool kKRing = kNB == 3 && kD == 128 && !kSparse && kSelect == kSelGiven;
+  constexpr bool kQInLds = kNB == 3 && !kKRing;
   bf16x8(*q_lds)[kD / 32][64] = nullptr;
   if constexpr (kQInLds) {
     __shared__ bf16x8 q_shared[kNB][kD / 32][64];
@@ -477,7 +572,81 @@ void attn_bf16_kernel(AttnArgs a) {
       w.physB = __builtin_amdgcn_readfirstlane(e.w);
       return w;
     };
-    if constexpr (kQInLds) {
+    if constexpr (kKRing) {
+      // Dense, head dim 128: K goes through this wave's own LDS ring by
+      // direct-to-LDS loads and V into registers, both kAhead windows ahead of
+      // the compute (32 KB in flight per wave). The wave reads only what it
+      // loaded, so its own vmcnt wait orders its reads; no barrier.
+      constexpr int kAhead = kKRingSlots - 1;
+      char* kring = region + k_ring_offset(a.pages_per_split);
+      int goff[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) goff[j] = k_dma_offset(j, lane);
+      int koff[2][kD / 32];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int c = 0; c < kD / 32; ++c) koff[mb][c] = k_lds_offset(mb, c, lane);
+      const size_t head_off = (size_t)h * kPage * kD;
+      const size_t page_stride = (size_t)a.Hkv * kPage * kD;
+      // The table is read back around loads in flight: ds_read_lone16.
+      auto pages_lone = [&](int wi) {
+        const int4 e = ds_read_lone16(win_tab + wi);
+        WindowPages w;
+        w.lpA = __builtin_amdgcn_readfirstlane(e.x);
+        w.lpB = __builtin_amdgcn_readfirstlane(e.y);
+        w.physA = __builtin_amdgcn_readfirstlane(e.z);
+        w.physB = __builtin_amdgcn_readfirstlane(e.w);
+        return w;
+      };
+      // Per window: V's kD/16 loads, then K's 8, in that order (a compiler
+      // barrier between them), so K(i) has landed once the 16 loads of each
+      // later window issued so far are all that remain in flight.
+      bf16x8 vt[kKRingSlots][kD / 16];
+      WindowPages wt[kKRingSlots];
+      auto issue = [&](int wi, int sl) {
+        wt[sl] = pages_lone(wi);
+        load_bf16_v<kD>(vt[sl], wt[sl], vp, a.Hkv, h);
+        asm volatile("" ::: "memory");
+        dma_k_window(kring + sl * 8192, kp, wt[sl].physA, wt[sl].physB, page_stride, head_off, goff);
+      };
+      // Every step issues one window, the split's last one again once past
+      // its end (into a slot nobody reads), so the same number of loads is in
+      // flight on every path. hipcc's wait analysis merges paths by load
+      // counts: with a step that issued nothing it would assume the V
+      // registers still pending and wait for every load at their first use.
+      wait_vm<0>();  // the table's page-table loads, before any load below is counted
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) issue(min(j, n_win - 1), j);
+      for (int base = 0; base < n_win; base += kKRingSlots) {
+#pragma unroll
+        for (int s = 0; s < kKRingSlots; ++s) {
+          const int i = base + s;
+          if (i >= n_win) break;
+          asm volatile("" ::: "memory");
+          wait_lgkm0();  // the reads of the slot refilled next are done
+          asm volatile("" ::: "memory");
+          issue(min(i + kAhead, n_win - 1), (s + kAhead) % kKRingSlots);
+          // K(i) (and V(i) before it) have landed once only the loads of the
+          // kAhead windows issued since remain.
+          asm volatile("" ::: "memory");
+          wait_vm<16 * kAhead>();
+          asm volatile("" ::: "memory");
+          const char* slot = kring + s * 8192;
+          bf16x8 k[2][kD / 32];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int c = 0; c < kD / 32; ++c) k[mb][c] = *reinterpret_cast<const bf16x8*>(slot + koff[mb][c]);
+          auto qsrc = [&](int nb, bf16x8 (&q)[kD / 32]) {
+#pragma unroll
+            for (int c = 0; c < kD / 32; ++c) q[c] = qb[nb][c];
+          };
+          compute_bf16_kv<kD, kNB>(k, vt[s], wt[s], qsrc, qpos, min_qpos, a.scale_log2, m_run, l_run, acc);
+        }
+      }
+      wait_vm<0>();  // the repeated tail loads land before the region takes the partial
+    } else if constexpr (kQInLds) {
       // K runs kDk = 2 windows ahead of the compute and V kDv = 1: 24 KB in
       // flight per wave, in the registers a third full stage would overflow.
       // The queries come from LDS.
@@ -594,44 +763,6 @@ void attn_bf16_kernel(AttnArgs a) {
 //      row at physical chunk c ^ (t % 16) ^ (4 * (t / 16)).
 //   V: page p (A, B) at 8192 + 4096 p; d at 32 d; token half e (0: tokens
 //      0..7, 1: 8..15) at physical half e ^ ((d / 8) % 2).
-constexpr int kStagedSlot = 16384;
-constexpr int kStagedLoads = 16;  // 1 KB loads per window
-
-template <int kCount>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(kCount >= 0 && kCount < 64, "vmcnt is 6 bits");
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14;
-  // expcnt and lgkmcnt left at their maxima (no wait).
-  __builtin_amdgcn_s_waitcnt((kCount & 15) | (7 << 4) | (15 << 8) | ((kCount >> 4) << 14));
-}
-
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// This wave's loads of a window before the barrier lets it be read: the
-// waves below kStagedLoads % kNB carry one load more.
-template <int kNB, int kAhead>
-__device__ __forceinline__ void wait_own_loads(int wave, bool full) {
-  constexpr int kLo = kStagedLoads / kNB, kHi = (kStagedLoads + kNB - 1) / kNB;
-  if (!full) {
-    wait_vm<0>();
-  } else if (wave < kStagedLoads % kNB) {
-    wait_vm<kAhead * kHi>();
-  } else {
-    wait_vm<kAhead * kLo>();
-  }
-}
-
-// One 8-byte LDS read that waits for itself (lgkmcnt(0)) in the same asm
-// block, and that the compiler therefore does not order against the
-// direct-to-LDS loads in flight.
-__device__ __forceinline__ uint64_t ds_read_lone(const void* p) {
-  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-  uint64_t r;
-  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
-  return r;
-}
 
 template <int kNB, int kR>
 __global__ __launch_bounds__(64 * kNB) void attn_bf16_staged_kernel(AttnArgs a) {
@@ -683,8 +814,7 @@ __global__ __launch_bounds__(64 * kNB) void attn_bf16_staged_kernel(AttnArgs a) 
     const int j = wave + kNB * i;
     const int page = (j & 7) >> 2;
     if (j < 8) {
-      const int rr = 4 * (j & 3) + (lane >> 4);
-      goff[i] = rr * kD + 8 * ((lane & 15) ^ rr ^ (4 * page));
+      goff[i] = k_dma_offset(j, lane);
     } else {
       const int d = 32 * (j & 3) + (lane >> 1);
       goff[i] = d * kPage + 8 * ((lane & 1) ^ ((d >> 3) & 1));
@@ -732,13 +862,9 @@ __global__ __launch_bounds__(64 * kNB) void attn_bf16_staged_kernel(AttnArgs a) 
   // This lane's LDS read offsets within a slot (see the layout above).
   int koff[2][kD / 32];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int pB = l16 >> 3;
-    const int tok = 8 * ((l16 >> 2) & 1) + 4 * mb + (l16 & 3);
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int s = 0; s < kD / 32; ++s)
-      koff[mb][s] = (16 * pB + tok) * 256 + 16 * ((4 * s + g4) ^ tok ^ (4 * pB));
-  }
+    for (int s = 0; s < kD / 32; ++s) koff[mb][s] = k_lds_offset(mb, s, lane);
   const int voff = 8192 + 4096 * (g4 >> 1) + 32 * l16 + 16 * ((g4 & 1) ^ ((l16 >> 3) & 1));
 
   float m_run[1] = {kNegInf}, l_run[1] = {0.f};
@@ -1139,6 +1265,10 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
   const long cap = ((long)max_items + 1) & ~1L;
   if (pps > cap) pps = cap;
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+  // Dense bf16 at head dim 128 with three row blocks: each wave's region also
+  // holds its K ring, after a window table of at most 8 KB.
+  const bool k_ring = dense && kv.kv_dtype == S3R_BF16 && kv.head_dim == 128 && p.row_blocks == 3;
+  if (k_ring && pps > 1024) pps = 1024;
   p.pages_per_split = (int32_t)pps;
   p.n_splits = (int32_t)((max_items + pps - 1) / pps);
   // bf16: the splits of one (sequence, kv head) run as the waves of one
@@ -1147,11 +1277,17 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
   const size_t table = sizeof(int) * 4 * (size_t)((pps + 1) / 2);
   const size_t partial = sizeof(float) * (size_t)p.rows * (kv.head_dim + 2);
   p.lds_region_bytes = (int32_t)(((table > partial ? table : partial) + 15) & ~(size_t)15);
+  size_t max_group_lds = kMaxGroupLds;
+  if (k_ring) {
+    const size_t ring_end = (size_t)k_ring_offset((int)pps) + kKRingBytes;
+    p.lds_region_bytes = (int32_t)(((ring_end > partial ? ring_end : partial) + 255) & ~(size_t)255);
+    max_group_lds = 160 * 1024;
+  }
   int w = 1;
   if (kv.kv_dtype == S3R_BF16) {
     const int wmax = p.row_blocks == 1 ? 8 : 4;
     while (w < wmax && w < p.n_splits) w *= 2;
-    while (w > 1 && (size_t)w * p.lds_region_bytes > kMaxGroupLds) w /= 2;
+    while (w > 1 && (size_t)w * p.lds_region_bytes > max_group_lds) w /= 2;
   }
   // Dense bf16, head dim 128, four row blocks: one split per workgroup, K/V
   // staged through LDS.
