@@ -1253,7 +1253,12 @@ SplitPlan plan_attention(const s3r_paged_kv& kv, int32_t n_queries, int32_t max_
   const int G = kv.num_q_heads / kv.num_kv_heads;
   p.rows = G * n_queries;
   p.row_blocks = (p.rows + 15) / 16;
-  const long kTargetItems = p.row_blocks == 1 ? 2048 : 1024;
+  // Two row blocks over few (sequence, kv head) pairs of unequal lengths (a
+  // ragged batch that has drained): four times the splits, so the long
+  // sequences' splits do not run on alone after the short ones finish.
+  const bool few_ragged = p.row_blocks == 2 && B * Hkv < 256 && kv.total_pages_hint > 0 &&
+                          4 * (long)kv.total_pages_hint < 3 * B * (long)kv.max_pages_per_seq;
+  const long kTargetItems = p.row_blocks == 1 ? 2048 : (few_ragged ? 4096 : 1024);
   long total = (long)B * max_items;
   if (kv.total_pages_hint > 0 && kv.total_pages_hint < total) total = kv.total_pages_hint;
   const double avg = (double)total / (double)B;
