@@ -168,6 +168,27 @@ def test_split_plan_workspace_scales_with_hint():
     assert hinted >= full  # a smaller average length means shorter splits, more of them
 
 
+def test_drained_two_row_block_verify_takes_finer_splits():
+    """A two-row-block verify over fewer than 256 (sequence, kv head) pairs whose
+    page hint is under 3/4 of B * max_pages (a drained ragged batch) targets
+    4096 splits instead of 1024. At 16 sequences x 8 kv heads, 4096 pages max,
+    hint 33697 pages, 20 rows: 2106 pages on average over 32 splits is 66 pages a
+    split, 63 splits, 16 groups of four waves; with the hint at B * max_pages the
+    same batch has 512-page splits, 8 splits, 2 groups. The workspace holds one
+    (rows x (D + 2)) fp32 partial per group."""
+    lib = _lib.load()
+    shape = dict(num_seqs=16, num_q_heads=32, num_kv_heads=8, head_dim=128, max_pages_per_seq=4096)
+    partial = 20 * (128 + 2) * 4
+    drained = lib.s3r_attn_workspace(ctypes.byref(_kv(total_pages_hint=33697, **shape)), 5, 4096)
+    uniform = lib.s3r_attn_workspace(ctypes.byref(_kv(total_pages_hint=16 * 4096, **shape)), 5, 4096)
+    assert drained == 16 * 8 * 16 * partial
+    assert uniform == 16 * 8 * 2 * partial
+    # 256 pairs (the Qwen3-8B batch) keep the usual target
+    big = dict(shape, num_seqs=32)
+    assert (lib.s3r_attn_workspace(ctypes.byref(_kv(total_pages_hint=32 * 2000, **big)), 5, 4096)
+            < 32 * 8 * 16 * partial)
+
+
 def test_ragged_hint_reserves_the_longest_first_order():
     """Once the page hint drops below half of B * max_pages (a ragged batch), the
     attention and draft-step workspaces also hold the sequence order: B int32,
