@@ -301,11 +301,14 @@ def test_determinism_bitwise():
     assert not torch.equal(o1[0], o3[0]) or not torch.equal(o1[1], o3[1])
 
 
-def test_split_count_invariance():
-    wl = _make(_cfg("bf16", 128, 4, 2, 6), [1500, 700], seed=22)
+@pytest.mark.parametrize("G,gamma", [(4, 6), (4, 8), (8, 7)], ids=["rows28", "rows36", "rows64"])
+def test_split_count_invariance(G, gamma):
+    """The page hint changes the split plan (register, K-ring and LDS-staged
+    pipelines alike), not the result."""
+    wl = _make(_cfg("bf16", 128, G, 2, gamma), [1500, 700], seed=22)
     outs = []
     for hint in (0, 200, 60):
-        kvc = _kv(wl, 6, hint=hint)
+        kvc = _kv(wl, gamma, hint=hint)
         outs.append(s3r.dense_verify_attn(kvc, wl.q_verify, 0.09).cpu())
     for o in outs[1:]:
         assert torch.max(torch.abs(o - outs[0])) <= 1e-5
@@ -538,12 +541,15 @@ def test_kv_commit_matches_oracle(kv, D, Hkv, ctx, count, slack, accepted):
     assert np.array_equal(f64(bounds), rB, equal_nan=True)
 
 
-def test_ragged_longest_first_matches_oracle():
+@pytest.mark.parametrize("G,gamma", [(4, 4), (4, 8), (8, 7)], ids=["rows20", "rows36", "rows64"])
+def test_ragged_longest_first_matches_oracle(G, gamma):
     """A ragged batch with its page hint set: the attention workgroups take the
-    sequences longest first (verify and the draft step)."""
+    sequences longest first (verify and the draft step), with the finer splits
+    of a batch of few pairs; 36 and 64 verify rows run the K-ring and the
+    LDS-staged pipelines."""
     ctx = (5000, 40, 700, 17, 2300, 64)
-    gamma, budget = 4, 256
-    wl = _make(_cfg("bf16", 128, 4, 2, gamma=gamma, budget=budget), list(ctx), seed=61)
+    budget = 256
+    wl = _make(_cfg("bf16", 128, G, 2, gamma=gamma, budget=budget), list(ctx), seed=61)
     total = sum(-(-(L + gamma) // 16) for L in ctx)
     assert wl.max_pages * len(ctx) > 2 * total  # ragged enough to reorder
     scale = 1.0 / np.sqrt(128)
