@@ -812,7 +812,6 @@ __global__ __launch_bounds__(64 * kNB) void attn_bf16_staged_kernel(AttnArgs a) 
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int j = wave + kNB * i;
-    const int page = (j & 7) >> 2;
     if (j < 8) {
       goff[i] = k_dma_offset(j, lane);
     } else {
