@@ -61,7 +61,7 @@ VERIFY_CASES = [
     ("bf16", 128, 4, 2, 6, (1000, 515, 129)),    # 28 rows: two row blocks (Qwen3-8B heads)
     ("bf16", 128, 4, 2, 8, (777, 64)),           # 36 rows: three row blocks
     ("bf16", 64, 8, 1, 7, (400, 95)),            # 64 rows: four row blocks, D=64
-    ("bf16", 128, 8, 1, 7, (300, 77)),           # 64 rows at D=128: the one-stage pipeline
+    ("bf16", 128, 8, 1, 7, (300, 77)),           # 64 rows at D=128: K/V staged through LDS
     ("bf16", 64, 2, 3, 3, (48, 2049)),
     # query groups that are not a power of two
     ("bf16", 128, 3, 2, 5, (500, 90)),           # 18 rows: two row blocks
@@ -353,9 +353,12 @@ def test_verify_row_equals_draft_over_all_pages():
         assert torch.max(torch.abs(dr - ver[:, i])) <= 1e-5
 
 
-def test_edge_cases_empty_and_short():
-    gamma = 4
-    wl = _make(_cfg("bf16", 128, 4, 2, gamma), [40, 3, 1], seed=25)
+@pytest.mark.parametrize("G,gamma", [(4, 4), (4, 8), (8, 7)], ids=["rows20", "rows36", "rows64"])
+def test_edge_cases_empty_and_short(G, gamma):
+    """An empty sequence, one shorter than the verify queries and a single
+    page, through the register (20 rows), K-ring (36) and LDS-staged (64)
+    verify pipelines."""
+    wl = _make(_cfg("bf16", 128, G, 2, gamma), [40, 3, 1], seed=25)
     seq = torch.tensor([0, 3, 16], dtype=torch.int32, device=DEV)  # empty, shorter than n_q, one page
     kvc = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, seq, wl.cfg["Hq"])
     out = s3r.dense_verify_attn(kvc, wl.q_verify, 0.1)
@@ -625,6 +628,37 @@ def test_very_long_context(hint):
     _check_attn(out, ref, "bf16")
     rd = oracle.sparse_draft_attn(f64(wl.draft_q(0)), K, V, pt, i32(wl.seq_lens[0]), sel, 0.125)
     _check_attn(d_out, rd, "bf16")
+
+
+def test_k_ring_verify_at_scale():
+    """36 verify rows over 512 (sequence, kv head) pairs of 40000 tokens (10 GB of
+    KV): the K-ring pipeline with splits long enough that the plan caps each
+    wave's window table at 1024 pages. Checked on every kv head of the first
+    and last sequences and on a seeded sample of the rest."""
+    gamma = 8
+    wl = make_workload("qwen3_8b", device=DEV, seed=5, with_logits=False, B=64, L=40000, gamma=gamma)
+    cfg = wl.cfg
+    B, Hq, Hkv, D, P = (cfg[k] for k in ("B", "Hq", "Hkv", "D", "P"))
+    assert (Hq // Hkv) * (gamma + 1) == 36
+    total = sum(-(-(int(L) + gamma) // P) for L in wl.ctx)
+    kv = s3r.PagedKVCache(wl.k_pool, wl.v_pool, wl.page_table, wl.seq_lens[gamma], Hq, total_pages_hint=total)
+    scale = 1.0 / np.sqrt(D)
+    out = s3r.dense_verify_attn(kv, wl.q_verify, scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    slices = sorted({(0, h) for h in range(Hkv)} | {(B - 1, h) for h in range(Hkv)} |
+                    {(int(b), int(h)) for b, h in zip(rng.integers(0, B, 4), rng.integers(0, Hkv, 4))})
+    G = Hq // Hkv
+    for b, h in slices:
+        n = -(-(int(wl.ctx[b]) + gamma) // P)
+        idx = wl.page_table[b, :n].long()
+        K = wl.k_pool.index_select(0, idx)[:, h:h + 1].to("cpu", torch.float64).numpy()
+        V = wl.v_pool.index_select(0, idx)[:, h:h + 1].to("cpu", torch.float64).numpy()
+        q = wl.q_verify[b:b + 1, :, h * G:(h + 1) * G].to("cpu", torch.float64).numpy()
+        ref = oracle.dense_verify_attn(q, K, V, np.arange(n, dtype=np.int64)[None, :],
+                                       np.array([int(wl.seq_lens[gamma][b])], dtype=np.int32), scale)
+        print(f"k-ring at scale: slice ({b}, {h})", flush=True)
+        _check_attn(out[b:b + 1, :, h * G:(h + 1) * G], ref, "bf16")
 
 
 def test_round_and_commit_edge_cases():
