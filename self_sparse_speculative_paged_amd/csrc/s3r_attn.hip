@@ -24,6 +24,13 @@
 // one 16-byte load. P is split into bf16 hi + lo parts so the P.V product keeps
 // ~16 mantissa bits. The fp32 path does the same on MFMA 16x16x4 f32, one page
 // per window.
+//
+// K/V windows reach the MFMAs through registers, loaded a few windows ahead of
+// the compute. Where a dense verify's accumulators leave too few registers for
+// that (head dim 128): at 33..48 rows each wave streams K through its own LDS
+// ring with direct-to-LDS loads and keeps V in registers; at 49..64 rows one
+// workgroup streams whole windows through a shared LDS ring, one wave per row
+// block (attn_bf16_staged_kernel).
 #include <climits>
 
 #include "s3r_common.h"
